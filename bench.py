@@ -1,0 +1,325 @@
+"""Benchmark of the FP8 wo_a hot path on one MI355X.
+
+One step = one pass of the wo_a path over an 8192-token prefill chunk
+(T = 8192, G = 16 groups, K = 4096 = 8 heads x 512, N = 1024): the fused
+inverse-RoPE + group-128 E8M0 FP8 quantiser, then the batched MX-scale FP8
+GEMM.  Inputs are seeded synthetic tensors resident in HBM before the timed
+region.  The headline value is the GEMM's FLOPs per step (2*T*G*N*K) divided
+by the step time, in TFLOP/s.
+
+Printed: one JSON line (the headline, with `roofline` for the GEMM --
+measured with HIP events on the stream the kernels run on -- and
+`cpu_baseline`, the CPU oracle timed on a bounded sample of the same
+workload), followed by secondary per-kernel records on stderr unless
+--json-extra is given, in which case they are folded into the JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--extra] [--long]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "wo_a fused quant+MX-FP8 bmm TFLOP/s at T=8192 (%FP8 peak); quant HBM GB/s"
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def quant_bytes(T, L, group=128):
+    """Algorithmic HBM bytes of the quantiser: BF16 in, FP8 out, one scale byte
+    per group, plus the per-token position and cos/sin row (R = 64)."""
+    return T * (L * 2 + L + L // group) + T * (8 + 2 * 64)
+
+
+def bmm_bytes(T, G, N, K):
+    """Algorithmic HBM bytes of one GEMM: A and its scales, W and its scales, BF16 out."""
+    return T * G * K + T * G * K // 128 + G * N * K + G * N * K // 128 + T * G * N * 2
+
+
+class Timer:
+    """HIP events recorded on the given torch stream (the stream the library launches on)."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def event(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        return e
+
+
+def bench_prefill(mx, torch, workloads, steps, warmup, fmt=0):
+    p = workloads.prefill_chunk()
+    cos, sin = workloads.rope_tables(rows=8192)
+    dev = torch.device("cuda:0")
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    x, cosd, sind = u16(p.x), u16(cos), u16(sin)
+    pos = torch.from_numpy(p.positions).to(dev)
+    w = torch.from_numpy(p.w).to(dev)
+    ws = torch.from_numpy(p.w_scale).to(dev)
+    L = p.H * p.D
+    q = torch.empty((p.T, L), dtype=torch.uint8, device=dev)
+    s = torch.empty((p.T, L // 128), dtype=torch.uint8, device=dev)
+    out = torch.empty((p.T, p.G, p.N), dtype=torch.bfloat16, device=dev)
+    qv, sv = q.view(p.T, p.G, p.K), s.view(p.T, p.G, p.K // 128)
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+
+    def step():
+        mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, 0, 128, fmt, q=q, scale=s)
+        mx.mx_bmm_a8w8_mxscale(qv, sv, w, ws, fmt, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = []
+    t_wall = time.perf_counter()
+    e0 = tm.event()
+    for _ in range(steps):
+        a = tm.event()
+        mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, 0, 128, fmt, q=q, scale=s)
+        b = tm.event()
+        mx.mx_bmm_a8w8_mxscale(qv, sv, w, ws, fmt, out=out)
+        c = tm.event()
+        marks.append((a, b, c))
+    e1 = tm.event()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    total_ms = e0.elapsed_time(e1)
+    q_ms = np.array([a.elapsed_time(b) for a, b, _ in marks])
+    b_ms = np.array([b.elapsed_time(c) for _, b, c in marks])
+    return dict(p=p, total_ms=total_ms, wall_s=wall, q_ms=q_ms, b_ms=b_ms, L=L)
+
+
+def cpu_baseline(workloads, tokens):
+    """The oracle (as it stands) on the first `tokens` tokens of the same chunk."""
+    from oracle.gemm import bmm_a8w8_mxscale
+    from oracle.quant import inv_rope_group_quant
+    p = workloads._big(1, 8192, False, "sample", x_rows=tokens)
+    cos, sin = workloads.rope_tables(rows=8192)
+    t0 = time.perf_counter()
+    rq, rs = inv_rope_group_quant(p.x, p.positions[:tokens], cos, sin, p.H, p.D, 64)
+    t1 = time.perf_counter()
+    bmm_a8w8_mxscale(rq.reshape(tokens, p.G, p.K), rs.reshape(tokens, p.G, -1), p.w, p.w_scale)
+    t2 = time.perf_counter()
+    flops = 2 * tokens * p.G * p.N * p.K
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    return {"value": flops / (t2 - t0) / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {tokens} of the 8192 tokens of the prefill chunk, all G/N/K; quant "
+                      f"{t1 - t0:.2f} s single-threaded numpy, fp64 GEMM {t2 - t1:.2f} s on BLAS "
+                      f"({threads} threads); host has {os.cpu_count()} CPUs, affinity "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def bench_extra(mx, torch, workloads, reps=50):
+    """Secondary per-kernel timings: decode batch (cold weights), MXFP8 linear,
+    dequantisation."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    res = {}
+
+    def timeit(fn, n=reps, between=None):
+        ts = []
+        for _ in range(3):
+            fn(0)
+        for i in range(n):
+            if between:
+                between(i)
+            a = tm.event()
+            fn(i)
+            b = tm.event()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        v = np.array([a.elapsed_time(b) for a, b in ts])
+        return float(np.median(v)) * 1e3, float(v.min()) * 1e3
+
+    # decode batch: T = 64 at random positions; 6 weight copies (384 MiB) rotate
+    # so that the 256 MB last-level cache cannot hold the weight (cold)
+    p = workloads.decode_batch()
+    cos, sin = workloads.rope_tables(rows=32768)
+    x, cosd, sind = u16(p.x), u16(cos), u16(sin)
+    pos = torch.from_numpy(p.positions).to(dev)
+    ws_copies = [(torch.from_numpy(p.w).to(dev), torch.from_numpy(p.w_scale).to(dev)) for _ in range(6)]
+    L = p.H * p.D
+    q = torch.empty((p.T, L), dtype=torch.uint8, device=dev)
+    s = torch.empty((p.T, L // 128), dtype=torch.uint8, device=dev)
+    out = torch.empty((p.T, p.G, p.N), dtype=torch.bfloat16, device=dev)
+    us_q, _ = timeit(lambda i: mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, q=q, scale=s))
+    us_b, us_b_min = timeit(lambda i: mx.mx_bmm_a8w8_mxscale(q.view(p.T, p.G, p.K), s.view(p.T, p.G, -1),
+                                                             ws_copies[i % 6][0], ws_copies[i % 6][1], out=out))
+    bb = bmm_bytes(p.T, p.G, p.N, p.K)
+    res["decode_T64"] = {"quant_us": us_q, "quant_GBps": quant_bytes(p.T, L) / us_q / 1e3,
+                         "bmm_us": us_b, "bmm_us_min": us_b_min, "bmm_GBps": bb / us_b / 1e3,
+                         "bmm_hbm_frac": bb / us_b / 1e3 / PEAK_HBM_GBS, "bmm_TFLOPs": p.flops / us_b / 1e6,
+                         "weights": "cold (6 rotating copies)"}
+    del ws_copies, x, q, s, out
+
+    # MXFP8 linear, M = 64, N = 4096: dequant at load for K % 128 != 0
+    data = workloads.mxfp8_linear()
+    lin = {}
+    for K, (xh, wh, wsh, _) in data.items():
+        xd, wd, wsd = u16(xh), torch.from_numpy(wh).to(dev), torch.from_numpy(wsh).to(dev)
+        M, N = xh.shape[0], wh.shape[0]
+        rec = {}
+        if K % 128:
+            us_dq, _ = timeit(lambda i: mx.mx_dequant_mxfp8_to_bf16(wd, wsd))
+            dq_bytes = N * K * (1 + 2) + N * K // 32
+            rec.update(dequant_us=us_dq, dequant_GBps=dq_bytes / us_dq / 1e3)
+            wprep = mx.mx_dequant_mxfp8_to_bf16(wd, wsd)
+            wbytes = N * K * 2
+        else:
+            wprep = wd
+            wbytes = N * K + N * K // 32
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        ws_t = torch.empty(max(1, mx.mx_linear_workspace_bytes(M, N, K, wprep.element_size())), dtype=torch.uint8,
+                           device=dev)
+        us_l, _ = timeit(lambda i: mx.mx_linear(xd, wprep, wsd, out=o, workspace=ws_t))
+        lbytes = wbytes + M * K * 2 + M * N * 2
+        rec.update(branch="bf16 (dequantised at load)" if K % 128 else "block-scaled fp8", linear_us=us_l,
+                   linear_GBps=lbytes / us_l / 1e3, linear_hbm_frac=lbytes / us_l / 1e3 / PEAK_HBM_GBS)
+        lin[f"K{K}"] = rec
+    res["mxfp8_linear_M64_N4096"] = lin
+    # the pages' production shape: 5120 x 576 shared-expert down_proj at TP4
+    rng = np.random.default_rng(21)
+    wd = torch.from_numpy(workloads.weight_codes(rng, (5120, 576))).to(dev)
+    wsd = torch.from_numpy(workloads.scale_bytes(rng, (5120, 18), -10, -4)).to(dev)
+    us_dq, _ = timeit(lambda i: mx.mx_dequant_mxfp8_to_bf16(wd, wsd))
+    res["dequant_5120x576"] = {"us": us_dq, "GBps": (5120 * 576 * 3 + 5120 * 18) / us_dq / 1e3,
+                               "algorithmic_bytes": 5120 * 576 * 3 + 5120 * 18}
+    return res
+
+
+def bench_long(mx, torch, workloads):
+    """The 100,000-token prefill streamed in 8192-token chunks (last 1,696),
+    quantiser + GEMM per chunk, OCP then FNUZ activations; activations are
+    generated on the GPU (seeded) and resident before timing."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+    cols, w, ws = workloads.long_prefill_weights()
+    wd, wsd = torch.from_numpy(w).to(dev), torch.from_numpy(ws).to(dev)
+    cos, sin = workloads.rope_tables()
+    cosd = torch.from_numpy(cos.view(np.int16)).to(dev)
+    sind = torch.from_numpy(sin.view(np.int16)).to(dev)
+    chunks = workloads.long_prefill_chunks()
+    xs = [workloads.device_activations(c, n, 65536, cols, dev) for c, (_, n) in enumerate(chunks)]
+    poss = [torch.arange(s0, s0 + n, dtype=torch.int64, device=dev) for s0, n in chunks]
+    H, D, G, N, K = 128, 512, 16, 1024, 4096
+    q = torch.empty((8192, H * D), dtype=torch.uint8, device=dev)
+    s = torch.empty((8192, H * D // 128), dtype=torch.uint8, device=dev)
+    out = torch.empty((8192, G, N), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for fmt, name in ((0, "ocp"), (1, "fnuz")):
+        def run():
+            for (s0, n), x, pos in zip(chunks, xs, poss):
+                mx.mx_inv_rope_group_quant(x, pos, cosd, sind, H, D, 64, 0, 128, fmt, q=q[:n], scale=s[:n])
+                mx.mx_bmm_a8w8_mxscale(q[:n].view(n, G, K), s[:n].view(n, G, K // 128), wd, wsd, fmt,
+                                       out=out[:n])
+        run()
+        torch.cuda.synchronize()
+        a = tm.event()
+        run()
+        b = tm.event()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        res[name] = {"ms": ms, "tokens_per_s": 1e5 / (ms / 1e3),
+                     "TFLOPs": 2 * 100_000 * G * N * K / (ms / 1e3) / 1e12}
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--extra", action="store_true", help="also time decode, MXFP8 linear, dequant")
+    ap.add_argument("--long", action="store_true", help="also time the 100,000-token chunked prefill")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (the wo_a path is measured on one MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mx_scaled_fp8_amd as mx
+    import workloads
+
+    mx.lib()
+    if not torch.cuda.is_available() or not mx.mx_probe(0):
+        print("bench.py: needs a gfx950 GPU and the built libmxfp8.so", file=sys.stderr)
+        sys.exit(1)
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; generating the prefill chunk")
+    r = bench_prefill(mx, torch, workloads, args.steps, args.warmup)
+    p = r["p"]
+    ms_step = r["total_ms"] / args.steps
+    tflops = p.flops / (ms_step / 1e3) / 1e12
+    b_avg_ms = float(r["b_ms"].mean())
+    q_avg_ms = float(r["q_ms"].mean())
+    b_ach = p.flops / (b_avg_ms / 1e3) / 1e12
+    qb = quant_bytes(p.T, r["L"])
+    q_gbs = qb / (q_avg_ms / 1e3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.1f} us: quant {q_avg_ms * 1e3:.1f} us ({q_gbs:.0f} GB/s), "
+        f"bmm {b_avg_ms * 1e3:.1f} us ({b_ach:.0f} TFLOP/s)")
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": p.name, "T": p.T, "G": p.G, "K": p.K, "N": p.N, "heads": p.H, "head_dim": p.D,
+                   "rope_dim": 64, "quant_group": 128, "fp8": "OCP e4m3 + E8M0", "parallelism": "single GPU"},
+        "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
+        "quant_hbm_GBps": round(q_gbs, 1),
+        "quant": {"us": round(q_avg_ms * 1e3, 2), "GBps": round(q_gbs, 1), "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+                  "algorithmic_bytes": qb},
+        "roofline": {"bound": "mfma", "kernel": "bmm_large_kernel", "achieved": round(b_ach, 1),
+                     "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(b_ach / PEAK_FP8_TFLOPS, 4),
+                     "launch_us": round(b_avg_ms * 1e3, 2), "algorithmic_flops": p.flops,
+                     "algorithmic_bytes": bmm_bytes(p.T, p.G, p.N, p.K), "traffic": None},
+        "wall_s_timed_region": round(r["wall_s"], 4),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle on {args.cpu_tokens} tokens")
+        rec["cpu_baseline"] = cpu_baseline(workloads, args.cpu_tokens)
+    if args.extra:
+        log("[bench] secondary kernels")
+        rec["kernels"] = bench_extra(mx, torch, workloads)
+    if args.long:
+        log("[bench] 100,000-token chunked prefill")
+        rec["long_prefill_100k"] = bench_long(mx, torch, workloads)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,121 @@
+// Internal helpers shared by the HIP sources of libmxfp8 (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mxfp8.h"
+
+namespace mx {
+
+// ------------------------------------------------------------------ host side
+
+// Records a printf-style message as the calling thread's last error and
+// returns `st`.
+mx_status fail(mx_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the calling thread's last error.
+void clear_error();
+// True when mx_set_dry_run(1) is in force.
+bool dry_run();
+// Checks that the current HIP device is a gfx950 (cached per device).
+mx_status require_gfx950();
+// Maps a launch error to MX_ERR_HIP with a message naming `what`.
+mx_status launch_status(const char* what);
+
+enum Counter {
+  C_QUANT = 0,
+  C_BMM_LARGE,
+  C_BMM_SMALL,
+  C_DEQUANT,
+  C_LINEAR_BF16,
+  C_LINEAR_FP8,
+  C_LINEAR_PERCALL,
+  C_E8M0_DEVICE,
+  C_E4M3_DEVICE,
+};
+void count(Counter c);
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Unsigned 32-bit division by a run-time constant d >= 1 through a 64-bit
+// multiply-high: q = mulhi64(n, ceil(2^64 / d)) is exact for every n < 2^32
+// (the rounding error of the reciprocal times n stays below 1/d).  d == 1 is
+// special-cased because 2^64 does not fit.
+struct DivU32 {
+  uint64_t magic;
+  uint32_t d;
+};
+inline DivU32 make_div(uint32_t d) {
+  DivU32 r;
+  r.d = d;
+  if (d <= 1) {
+    r.magic = 0;
+  } else {
+    // ceil(2^64 / d) = floor((2^64 - 1) / d) + 1 for d not dividing 2^64 - 1 ... and
+    // in general floor((2^64-1)/d) + 1 >= 2^64/d with error < 1.
+    r.magic = ~uint64_t(0) / d + 1;
+  }
+  return r;
+}
+
+// ---------------------------------------------------------------- device side
+
+__device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 dv) {
+  return dv.magic == 0 ? n : static_cast<uint32_t>(__umul64hi(static_cast<uint64_t>(n), dv.magic));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float32 -> BF16 bits, round to nearest even on the bit pattern; NaN stays a
+// quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Scale exponent of a group from the BF16 pattern of its amax (sign cleared):
+// e = ceil(log2(amax / M)) with M = 1.75 * 2^EM (EM = 8 for 448, 7 for 224).
+// Writing amax = m * 2^E with m in [1, 2): e = E - EM + (m > 1.75), because
+// M * 2^(E-EM) = 1.75 * 2^E.  On BF16 bits m > 1.75 means mantissa field > 0x60.
+// Clamped to [-127, 127]; 0 gives -127.  amax must be finite (< 0x7F80).
+template <int EM>
+__device__ __forceinline__ int e8m0_exponent(uint32_t amax_bits) {
+  const int ef = static_cast<int>(amax_bits >> 7);
+  const int mf = static_cast<int>(amax_bits & 0x7F);
+  int E, over;
+  if (ef != 0) {
+    E = ef - 127;
+    over = mf > 0x60;
+  } else {
+    // subnormal (or zero): value mf * 2^-133
+    const int bl = 32 - __clz(mf);              // bit length, 0 for zero
+    E = bl - 1 - 133;
+    over = ((mf << (8 - bl)) & 0x7F) > 0x60;
+  }
+  int e = E - EM + over;
+  if (amax_bits == 0) e = -127;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Two floats -> two OCP e4m3 codes (round to nearest even) packed into the low
+// (HI = false) or high (HI = true) 16 bits of `old`.  Inputs must be within
+// [-448, 448] or NaN.
+template <bool HI>
+__device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// In each byte of `w`, turn 0x80 (OCP -0) into 0x00 (FNUZ has no -0).
+__device__ __forceinline__ uint32_t ocp_negzero_to_fnuz(uint32_t w) {
+  const uint32_t t = w ^ 0x80808080u;                              // 0x80 bytes -> 0
+  const uint32_t nz = (((t & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | t) & 0x80808080u;  // high bit: byte != 0
+  return w ^ (~nz & 0x80808080u);
+}
+
+}  // namespace mx

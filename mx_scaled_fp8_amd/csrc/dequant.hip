@@ -1,0 +1,120 @@
+// One-pass MXFP8 -> BF16 weight dequantisation, and the device format
+// converters (gfx950).
+//
+// "[ROCm][DSv4.1][Perf] Dequantize the MXFP8 weight once when dot_scaled
+// cannot be used" (Purpose; "Why it is worth a patch"): out[n,k] =
+// bf16(decode(w[n,k]) * 2^(s[n,k/block]-127)).  The page's version chains
+// pointwise kernels through an FP32 intermediate; here every lane reads 16
+// codes (16 bytes) and one scale byte and writes 16 BF16 (32 bytes), so the
+// pass moves 1 + 1/block + 2 bytes per element and nothing else.  The product
+// of an e4m3 value (4 significant bits) and a power of two is exact in FP32
+// down to 2^-136, so the only rounding is the final nearest-even to BF16.
+#include "common.hpp"
+
+namespace mx {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool HI_WORD>
+__device__ __forceinline__ uint32_t dq_pair(uint32_t codes, int e, bool nan_scale) {
+  const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes), HI_WORD);
+  float a = ldexpf(f[0], e), b = ldexpf(f[1], e);
+  if (nan_scale) { a = __builtin_nanf(""); b = a; }
+  return pack_bf16x2(a, b);
+}
+
+__global__ __launch_bounds__(kThreads) void dequant_kernel(const uint4* __restrict__ w, const uint8_t* __restrict__ sc,
+                                                           uint4* __restrict__ out, uint64_t chunks,
+                                                           uint32_t chunks_per_block_shift) {
+  const uint64_t c = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (c >= chunks) return;
+  const uint4 v = w[c];
+  const uint32_t s = sc[c >> chunks_per_block_shift];
+  const int e = static_cast<int>(s) - 127;
+  const bool nan_scale = s == 0xFFu;
+  uint4 o0, o1;
+  o0.x = dq_pair<false>(v.x, e, nan_scale);
+  o0.y = dq_pair<true>(v.x, e, nan_scale);
+  o0.z = dq_pair<false>(v.y, e, nan_scale);
+  o0.w = dq_pair<true>(v.y, e, nan_scale);
+  o1.x = dq_pair<false>(v.z, e, nan_scale);
+  o1.y = dq_pair<true>(v.z, e, nan_scale);
+  o1.z = dq_pair<false>(v.w, e, nan_scale);
+  o1.w = dq_pair<true>(v.w, e, nan_scale);
+  out[2 * c] = o0;
+  out[2 * c + 1] = o1;
+}
+
+// FP32 power of two 2^n, -127 <= n <= 127 -> byte n + 127; else 0xFF and counted.
+__global__ __launch_bounds__(kThreads) void f32_to_e8m0_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                               uint64_t n, int32_t* reject_count) {
+  const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t u = __float_as_uint(in[i]);
+  const uint32_t ef = (u >> 23) & 0xFFu;
+  int b;
+  if (u == 0x00400000u) b = 0;
+  else if ((u >> 31) != 0 || (u & 0x7FFFFFu) != 0 || ef == 0 || ef == 0xFFu) b = -1;
+  else b = static_cast<int>(ef);
+  if (b < 0) {
+    out[i] = 0xFF;
+    if (reject_count) atomicAdd(reject_count, 1);
+  } else {
+    out[i] = static_cast<uint8_t>(b);
+  }
+}
+
+// FP32 -> e4m3, nearest even, saturating.  The FNUZ code of v is the OCP
+// code of 2v (the FNUZ grid is the OCP grid halved, 224 = 448 / 2) with -0
+// mapped to 0x00.
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void f32_to_e4m3_kernel(const float* __restrict__ in, uint8_t* __restrict__ out,
+                                                               uint64_t n) {
+  const uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n) return;
+  float v = in[i];
+  uint32_t code;
+  if (__builtin_isnan(v)) {
+    code = FMT == MX_FP8_E4M3_OCP ? 0x7Fu : 0x80u;
+  } else {
+    if (FMT == MX_FP8_E4M3_FNUZ) v = ldexpf(v, 1);     // exact, or +-Inf
+    v = fminf(fmaxf(v, -448.0f), 448.0f);                // saturate (Inf included)
+    code = static_cast<uint32_t>(cvt_fp8x2<false>(v, v, 0)) & 0xFFu;
+    if (FMT == MX_FP8_E4M3_FNUZ && code == 0x80u) code = 0;
+  }
+  out[i] = static_cast<uint8_t>(code);
+}
+
+}  // namespace
+
+mx_status launch_dequant(const uint8_t* w, const uint8_t* w_scale, void* out, int64_t N, int64_t K, int32_t block,
+                         hipStream_t stream) {
+  const uint64_t chunks = static_cast<uint64_t>(N) * static_cast<uint64_t>(K) / 16;
+  if (chunks == 0) return MX_OK;
+  const uint32_t shift = block == 32 ? 1 : 3;   // 16-code chunks per scale block: 2 or 8
+  const uint64_t blocks = (chunks + kThreads - 1) / kThreads;
+  dequant_kernel<<<static_cast<uint32_t>(blocks), kThreads, 0, stream>>>(
+      reinterpret_cast<const uint4*>(w), w_scale, reinterpret_cast<uint4*>(out), chunks, shift);
+  return launch_status("mx_dequant_mxfp8_to_bf16");
+}
+
+mx_status launch_f32_to_e8m0(const float* in, uint8_t* out, int64_t n, int32_t* reject_count, hipStream_t stream) {
+  if (n == 0) return MX_OK;
+  const uint64_t blocks = (static_cast<uint64_t>(n) + kThreads - 1) / kThreads;
+  f32_to_e8m0_kernel<<<static_cast<uint32_t>(blocks), kThreads, 0, stream>>>(in, out, n, reject_count);
+  return launch_status("mx_f32_pow2_to_e8m0_device");
+}
+
+mx_status launch_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, int32_t fmt, hipStream_t stream) {
+  if (n == 0) return MX_OK;
+  const uint64_t blocks = (static_cast<uint64_t>(n) + kThreads - 1) / kThreads;
+  if (fmt == MX_FP8_E4M3_OCP)
+    f32_to_e4m3_kernel<MX_FP8_E4M3_OCP><<<static_cast<uint32_t>(blocks), kThreads, 0, stream>>>(in, out, n);
+  else
+    f32_to_e4m3_kernel<MX_FP8_E4M3_FNUZ><<<static_cast<uint32_t>(blocks), kThreads, 0, stream>>>(in, out, n);
+  return launch_status("mx_f32_to_e4m3_device");
+}
+
+}  // namespace mx

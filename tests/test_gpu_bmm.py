@@ -1,0 +1,122 @@
+"""GPU parity of mx_bmm_a8w8_mxscale against the fp64 oracle.
+
+Bound: |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref).  Cases: the tiny wo_a
+problem end to end (quantiser then GEMM), stand-alone random operands over
+tile-crossing and ragged shapes for both kernels (T <= 64 and larger), FNUZ
+activations (and their bit-identity with the OCP run of the same values), the
+decode batch and the 8192-token prefill chunk at full size with sampled rows
+checked, and run-to-run determinism.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mx_scaled_fp8_amd as mx
+import workloads
+from helpers import assert_gemm_close, dev_i64, dev_u16, dev_u8, host_u16, requires_gpu, say
+from oracle import formats as F
+from oracle import gemm as G
+from oracle.quant import inv_rope_group_quant
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _gpu_bmm(a, sa, w, sw, fmt=mx.MX_FP8_E4M3_OCP):
+    out = mx.mx_bmm_a8w8_mxscale(dev_u8(a), dev_u8(sa), dev_u8(w), dev_u8(sw), fmt)
+    torch.cuda.synchronize()
+    return host_u16(out)
+
+
+def test_tiny_end_to_end():
+    p = workloads.tiny()
+    cos, sin = workloads.rope_tables(rows=64)
+    say("bmm tiny end to end")
+    q, s = mx.mx_inv_rope_group_quant(dev_u16(p.x), dev_i64(p.positions), dev_u16(cos), dev_u16(sin),
+                                      p.H, p.D, 64)
+    out = mx.mx_bmm_a8w8_mxscale(q.view(p.T, p.G, p.K), s.view(p.T, p.G, p.K // 128), dev_u8(p.w),
+                                 dev_u8(p.w_scale))
+    torch.cuda.synchronize()
+    rq, rs = inv_rope_group_quant(p.x, p.positions, cos, sin, p.H, p.D, 64)
+    ref = G.bmm_a8w8_mxscale(rq.reshape(p.T, p.G, p.K), rs.reshape(p.T, p.G, -1), p.w, p.w_scale)
+    assert_gemm_close(host_u16(out), ref, "tiny")
+
+
+SHAPES = [
+    # T, G, N, K  -- small-T kernel (T <= 64) and the large-tile kernel
+    (1, 1, 16, 128), (7, 2, 48, 256), (64, 3, 128, 512), (16, 2, 128, 256),
+    (65, 1, 16, 128), (200, 2, 272, 384), (256, 1, 256, 128), (300, 3, 512, 640), (513, 2, 784, 256),
+]
+
+
+@pytest.mark.parametrize("T,Gn,N,K", SHAPES)
+def test_random_operands(T, Gn, N, K):
+    a, sa, w, sw = workloads.gemm_operands(1000 + T + N, T, Gn, N, K)
+    say("bmm random", T, Gn, N, K)
+    out = _gpu_bmm(a, sa, w, sw)
+    ref = G.bmm_a8w8_mxscale(a, sa, w, sw)
+    assert_gemm_close(out, ref, f"T={T} G={Gn} N={N} K={K}")
+
+
+@pytest.mark.parametrize("T", [40, 300])
+def test_fnuz_activations(T):
+    Gn, N, K = 2, 256, 512
+    a, sa, w, sw = workloads.gemm_operands(77 + T, T, Gn, N, K, a_exp=(-12, -2))
+    # the same values in FNUZ: code unchanged, scale + 1, -0 -> 0
+    a_fnuz = np.where(a == 0x80, 0, a).astype(np.uint8)
+    sa_fnuz = (sa.astype(int) + 1).astype(np.uint8)
+    say("bmm fnuz", T)
+    o_ocp = _gpu_bmm(a, sa, w, sw)
+    o_fnuz = _gpu_bmm(a_fnuz, sa_fnuz, w, sw, mx.MX_FP8_E4M3_FNUZ)
+    ref = G.bmm_a8w8_mxscale(a_fnuz, sa_fnuz, w, sw, a_fmt=F.FNUZ)
+    assert_gemm_close(o_fnuz, ref, "fnuz")
+    assert np.array_equal(o_ocp, o_fnuz)
+
+
+def test_deterministic():
+    a, sa, w, sw = workloads.gemm_operands(5, 300, 2, 512, 512)
+    assert np.array_equal(_gpu_bmm(a, sa, w, sw), _gpu_bmm(a, sa, w, sw))
+
+
+def test_special_scales():
+    """E8M0 0xFF scales make their block NaN; scale byte 0 (2^-127) is honoured."""
+    T, Gn, N, K = 32, 1, 32, 256
+    a, sa, w, sw = workloads.gemm_operands(9, T, Gn, N, K)
+    sa[0, 0, 1] = 0xFF
+    out = F.bf16_to_f64(_gpu_bmm(a, sa, w, sw))
+    assert np.all(np.isnan(out[0, 0, :]))
+    assert not np.isnan(out[1:]).any()
+
+
+def _sampled_check(p, q_dev, s_dev, rows, what):
+    out = mx.mx_bmm_a8w8_mxscale(q_dev.view(p.T, p.G, p.K), s_dev.view(p.T, p.G, p.K // 128), dev_u8(p.w),
+                                 dev_u8(p.w_scale))
+    torch.cuda.synchronize()
+    return host_u16(out)[rows]
+
+
+def test_decode_batch_full_size():
+    p = workloads.decode_batch()
+    cos, sin = workloads.rope_tables(rows=32768)
+    say("bmm decode batch")
+    q, s = mx.mx_inv_rope_group_quant(dev_u16(p.x), dev_i64(p.positions), dev_u16(cos), dev_u16(sin),
+                                      p.H, p.D, 64)
+    rows = np.arange(p.T)
+    out = _sampled_check(p, q, s, rows, "decode")
+    rq, rs = inv_rope_group_quant(p.x, p.positions, cos, sin, p.H, p.D, 64)
+    ref = G.bmm_a8w8_mxscale(rq.reshape(p.T, p.G, p.K), rs.reshape(p.T, p.G, -1), p.w, p.w_scale)
+    assert_gemm_close(out, ref, "decode")
+
+
+@pytest.mark.slow
+def test_prefill_chunk_sampled_rows():
+    p = workloads.prefill_chunk()
+    cos, sin = workloads.rope_tables(rows=8192)
+    say("bmm prefill chunk T=8192")
+    q, s = mx.mx_inv_rope_group_quant(dev_u16(p.x), dev_i64(p.positions), dev_u16(cos), dev_u16(sin),
+                                      p.H, p.D, 64)
+    rows = np.unique(np.concatenate([[0, 255, 256, 8191], np.random.default_rng(12).integers(0, 8192, 28)]))
+    out = _sampled_check(p, q, s, rows, "prefill")
+    rq, rs = inv_rope_group_quant(p.x[rows], p.positions[rows], cos, sin, p.H, p.D, 64)
+    ref = G.bmm_a8w8_mxscale(rq.reshape(len(rows), p.G, p.K), rs.reshape(len(rows), p.G, -1), p.w, p.w_scale)
+    assert_gemm_close(out, ref, "prefill")

@@ -1,0 +1,118 @@
+"""GPU parity of the MXFP8 dequantiser and the MXFP8 linear.
+
+* Dequantisation is bit-exact against the oracle (the product of an e4m3
+  value and a power of two is exact, only the BF16 rounding remains), for the
+  linear's K = 288 / 576 and the pages' 5120 x 576 production shape.
+* mx_linear on every K of the MXFP8-linear workload: the BF16 branch on a
+  weight dequantised at load (K = 288, 576), the block-scaled FP8 branch
+  (K = 1152, 2304), within the GEMM bound of the matching oracle branch.
+* The unaligned FP8 weight that was not prepared takes the per-call
+  dequantisation branch: its output equals the load-time branch bit for bit,
+  and the launch counters show that the scaled GEMM was never reached (the
+  review thread of the MXFP8 page asks for exactly these two checks).
+* The converter turns the FP32 power-of-two scales into the same E8M0 bytes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import mx_scaled_fp8_amd as mx
+import workloads
+from helpers import assert_gemm_close, dev_u16, dev_u8, host_u16, requires_gpu, say
+from oracle import formats as F
+from oracle import gemm as G
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+@pytest.fixture(scope="module")
+def data():
+    return workloads.mxfp8_linear()
+
+
+@pytest.mark.parametrize("K", [288, 576])
+def test_dequant_bit_exact(data, K):
+    _, w, ws, _ = data[K]
+    say("dequant", K)
+    out = host_u16(mx.mx_dequant_mxfp8_to_bf16(dev_u8(w), dev_u8(ws)))
+    assert np.array_equal(out, G.dequant_mxfp8_to_bf16(w, ws, 32))
+
+
+def test_dequant_production_shape():
+    rng = np.random.default_rng(21)
+    w = workloads.weight_codes(rng, (5120, 576))
+    ws = workloads.scale_bytes(rng, (5120, 18), -10, -4)
+    out = host_u16(mx.mx_dequant_mxfp8_to_bf16(dev_u8(w), dev_u8(ws)))
+    assert np.array_equal(out, G.dequant_mxfp8_to_bf16(w, ws, 32))
+
+
+def test_dequant_block128_and_nan():
+    rng = np.random.default_rng(22)
+    w = workloads.weight_codes(rng, (64, 256))
+    w[0, 0] = 0x7F
+    ws = workloads.scale_bytes(rng, (64, 2), -10, 10)
+    ws[1, 1] = 0xFF
+    out = host_u16(mx.mx_dequant_mxfp8_to_bf16(dev_u8(w), dev_u8(ws), block=128))
+    ref = G.dequant_mxfp8_to_bf16(w, ws, 128)
+    nan = np.isnan(F.bf16_to_f64(ref))
+    assert np.array_equal(np.isnan(F.bf16_to_f64(out)), nan) and nan.sum() == 1 + 128
+    assert np.array_equal(out[~nan], ref[~nan])
+
+
+@pytest.mark.parametrize("K", workloads.LINEAR_KS)
+def test_linear_each_k(data, K):
+    x, w, ws, ws_f32 = data[K]
+    # load time: FP32 power-of-two scales -> E8M0 (host converter), then
+    # dequantise once iff K % 128 != 0
+    sb, ok = mx.mx_f32_pow2_to_e8m0(ws_f32)
+    assert ok and np.array_equal(sb, ws)
+    dw = dev_u8(w)
+    dws = dev_u8(sb)
+    prepared = mx.mx_dequant_mxfp8_to_bf16(dw, dws) if mx.mx_linear_dequant_at_load(K) else dw
+    mx.mx_reset_counters()
+    say("mx_linear", K)
+    out = host_u16(mx.mx_linear(dev_u16(x), prepared, dws))
+    c = mx.mx_get_counters()
+    ref = G.mx_linear(x, w, ws, 32)
+    assert_gemm_close(out, ref, f"K={K}")
+    if K % 128:
+        assert c["linear_bf16"] == 1 and c["linear_fp8"] == 0
+    else:
+        assert c["linear_fp8"] == 1 and c["linear_bf16"] == 0
+
+
+@pytest.mark.parametrize("K", [288, 576])
+def test_unprepared_unaligned_weight_never_reaches_scaled_gemm(data, K):
+    x, w, ws, _ = data[K]
+    dx, dw, dws = dev_u16(x), dev_u8(w), dev_u8(ws)
+    loaded = mx.mx_linear(dx, mx.mx_dequant_mxfp8_to_bf16(dw, dws), dws)
+    mx.mx_reset_counters()
+    say("mx_linear per-call dequant", K)
+    percall = mx.mx_linear(dx, dw, dws)
+    c = mx.mx_get_counters()
+    assert c["linear_percall_dequant"] == 1 and c["linear_fp8"] == 0
+    assert np.array_equal(host_u16(percall), host_u16(loaded))
+
+
+def test_aligned_control_k2048():
+    """K = 2048 is the aligned control that keeps reaching the scaled path."""
+    rng = np.random.default_rng(23)
+    x = workloads.activations(rng, 64, 2048)
+    w = workloads.weight_codes(rng, (256, 2048))
+    ws = workloads.scale_bytes(rng, (256, 64), -10, -4)
+    mx.mx_reset_counters()
+    out = host_u16(mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws)))
+    assert mx.mx_get_counters()["linear_fp8"] == 1
+    assert_gemm_close(out, G.mx_linear(x, w, ws, 32), "K=2048")
+
+
+@pytest.mark.parametrize("M", [1, 5, 64])
+def test_linear_small_m(M):
+    rng = np.random.default_rng(30 + M)
+    for K in (288, 1152):
+        x = workloads.activations(rng, M, K)
+        w = workloads.weight_codes(rng, (128, K))
+        ws = workloads.scale_bytes(rng, (128, K // 32), -10, -4)
+        out = host_u16(mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws)))
+        assert_gemm_close(out, G.mx_linear(x, w, ws, 32), f"M={M} K={K}")

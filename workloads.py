@@ -20,8 +20,11 @@ Draw order is part of the recipe (numpy ``default_rng``, PCG64):
   (64, K) std normal; W codes (4096, K); scale exponents (4096, K/32) in
   [-10, -4].
 * long prefill (seed 4): outlier columns, W codes and scale exponents as the
-  prefill chunk; chunk c's activations come from ``default_rng([4, c])``.
-  100,000 tokens = 12 chunks of 8192 + one of 1,696; positions 8192c + i.
+  prefill chunk.  100,000 tokens = 12 chunks of 8192 + one of 1,696;
+  positions 8192c + i.  Chunk c's activations are drawn on the GPU with
+  torch's Philox generator seeded 4000 + c (13 GiB of BF16 would take minutes
+  to draw on the host), std normal, outlier columns x 20, rounded to BF16;
+  tests copy the rows they check back to the host for the oracle.
 
 The rotary tables are the usual ones: omega_i = theta**(-2i/rope_dim), angle =
 pos * omega_i in fp64, cos/sin rounded to float32 and then to BF16.
@@ -160,12 +163,14 @@ def long_prefill_chunks(total=LONG_TOKENS, chunk=CHUNK):
     return out
 
 
-def long_prefill_chunk(c, cols, rows=None):
-    """Activations of chunk c (BF16 bits) and its positions."""
-    start, n = long_prefill_chunks()[c]
-    rng = np.random.default_rng([4, c])
-    x = activations(rng, n if rows is None else rows, 128 * 512, cols)
-    return x, np.arange(start, start + (n if rows is None else rows), dtype=np.int64)
+def device_activations(c, T, width, outlier_cols, device):
+    """Chunk c of the long prefill, drawn on `device`: BF16 [T, width] as int16 bits."""
+    g = torch.Generator(device=device)
+    g.manual_seed(4000 + c)
+    x = torch.randn((T, width), generator=g, device=device, dtype=torch.float32)
+    cols = torch.as_tensor(np.asarray(outlier_cols), device=device)
+    x[:, cols] *= 20.0
+    return x.to(torch.bfloat16).view(torch.int16)
 
 
 def gemm_operands(seed, T, G, N, K, a_exp=(-12, -2), w_exp=(-8, -4)):
