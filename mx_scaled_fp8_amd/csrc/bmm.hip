@@ -35,6 +35,8 @@
 //  * small-T (T <= 64, decode and the MXFP8 linear): one workgroup per
 //    (g, 16*NT n) with all T rows; the 4 waves split K and reduce through LDS.
 //    Operands stream straight from global memory (weight-bandwidth bound).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace mx {
@@ -66,16 +68,29 @@ __device__ __forceinline__ uint2 pack4_bf16(const v4f& v) {
 }
 
 // ------------------------------------------------------------- large tiles
+//
+// 256 (t) x 256 (n) workgroup tile, 4 waves of 128 x 128, on
+// v_mfma_scale_f32_32x32x64_f8f6f4 (4 x 4 MFMA tiles per wave, accumulators
+// in AGPRs).  K advances 128 bytes per stage, so every row of a tile is read
+// from L2 as whole 128-byte lines (64-byte pieces cost a quarter of the L2 to
+// CU bandwidth).  Two stages live in LDS as separate __shared__ arrays and the
+// stage loop is unrolled by two, so every access names its buffer statically
+// and the compiler can see that the DMA filling the other stage does not alias
+// the fragments being read.  Inside a stage the two 64-K halves are double
+// buffered in registers: the reads of the second half overlap the MFMAs of
+// the first.
 
-constexpr int kLT = 256;            // tile rows along t
-constexpr int kLN = 256;            // tile rows along n
-constexpr int kBK = 128;            // K bytes per step
-constexpr int kRowChunks = kBK / 16;
-constexpr int kTileBytes = kLT * kBK;   // 32 KiB per operand per stage
+constexpr int kLT = 256;                 // tile rows along t
+constexpr int kLN = 256;                 // tile rows along n
+constexpr int kBK = 128;                 // K bytes per stage = one scale group
+constexpr int kOpBytes = kLT * kBK;      // 32 KiB per operand per stage
+constexpr int kScaleWin = 32;            // stages whose scales are staged in LDS at once
 
-// physical 16-byte chunk of logical chunk c in row r: conflict free for 8
-// consecutive rows (32 banks) and for 16 consecutive rows (64 banks)
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// physical 16-byte chunk of logical chunk c in a 128-byte row r is c ^ swz8(r):
+// conflict free for 8 consecutive rows (32 banks) and for 16 (64 banks)
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
 
 struct LargeArgs {
   const uint8_t* a;      // [T, G, K]
@@ -87,14 +102,14 @@ struct LargeArgs {
   int tiles_t, tiles_n, total_tiles, per_xcd;
 };
 
-constexpr int kScaleWin = 32;    // K-steps whose scales are staged in LDS at once
-
 template <bool A_FNUZ>
 __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2][kTileBytes];   // [stage][W|A]
-  // scales of a window of K-steps, [step][W|A][wave half][row % 16][row / 16 % 8]:
-  // one 8-byte read gives a lane the scales of its 8 tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kScaleWin][2][2][16][8];
+  // stage buffers: [W tile 256 x 128 B | A tile 256 x 128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kOpBytes];
+  // scales of a window of stages, [stage][W|A][wave half][row % 32][tile]:
+  // one 4-byte read gives a lane the scales of its 4 tiles of one operand
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kScaleWin][2][2][32][4];
 
   // XCD-aware work id: workgroup i runs on XCD i % 8
   const int xcd = blockIdx.x & 7;
@@ -109,124 +124,186 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wn = wave & 1, wt = wave >> 1;     // wave's 128x128 sub-tile
-  const int KB = p.K / kBK;
+  const int KB = p.K / kBK;                    // stages
+  // each tile starts its K loop at a different stage, so that the workgroups
+  // sharing an XCD do not all stream the same K offset at once (when the
+  // whole K fits one scale window; otherwise from 0)
+  const int kb0 = KB <= kScaleWin ? work % KB : 0;
   const uint32_t rowA = static_cast<uint32_t>(p.G) * p.K;   // activation row stride
 
-  // LDS-DMA sources, relative to the tile's first row: wave `wave` fills
-  // rows it*32 + wave*8 + lane/8 of each operand tile (it = 0..7), lane i ->
-  // physical chunk i%8.  Rows past T or N re-read the last valid row.
+  // LDS-DMA sources: wave `wave` fills rows it*32 + wave*8 + lane/8 (it =
+  // 0..7) of each operand tile, lane i -> physical chunk i%8; rows past T or
+  // N re-read the last valid row
   const uint8_t* baseW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
   const uint8_t* baseA = p.a + static_cast<size_t>(t0) * rowA + static_cast<size_t>(g) * p.K;
   const int dma_row = wave * 8 + (lane >> 3);
-  const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz(dma_row)) * 16;   // swz(r) = swz(r % 16)
+  const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz8(dma_row)) * 16;   // swz8(r) = swz8(r % 16)
   const int limW = p.N - 1 - n0, limA = p.T - 1 - t0;
-
-  // operand reads inside a stage: row wn*128 + i*16 + lane%16; the swizzle
-  // only depends on row % 16, so tile i sits at +i*16 rows
-  // (lane group q reads the 16-byte chunks q and q + 4: K [16q, 16q+16) and
-  // [64+16q, 64+16q+16), the hardware's operand order)
-  const int r16 = lane & 15;
-  const int q4 = lane >> 4;
-  const int rdW = (wn * 128 + r16) * kBK;
-  const int rdA = (wt * 128 + r16) * kBK;
-  const int ch0 = (q4 ^ swz(r16)) << 4;
-  const int ch1 = ((q4 + 4) ^ swz(r16)) << 4;
-
-  // thread `tid` stages the scales of W row tid and A row tid
-  const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
-  const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * KB;
-  uint8_t* sc_dst = &lds_sc[0][0][tid >> 7][tid & 15][(tid >> 4) & 7];
-  constexpr int kScStep = 2 * 2 * 16 * 8;     // bytes per step in lds_sc
-  constexpr int kScOp = 2 * 16 * 8;           // W -> A offset
-
-  v4f acc[8][8];
+  uint32_t offW[8], offA[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  auto issue = [&](int kt, int stage) {
-    const uint32_t koff = static_cast<uint32_t>(kt) * kBK + dma_chunk;
+  for (int it = 0; it < 8; ++it) {
+    const int r = it * 32 + dma_row;
+    offW[it] = static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + dma_chunk;
+    offA[it] = static_cast<uint32_t>(min(r, limA)) * rowA + dma_chunk;
+  }
+  auto issue = [&](uint8_t* buf, int kb) {   // kb >= KB re-reads the last stage (harmless)
+    int kr = min(kb, KB - 1) + kb0;
+    kr -= kr >= KB ? KB : 0;
+    const uint32_t koff = static_cast<uint32_t>(kr) * kBK;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int r = it * 32 + dma_row;
-      const uint8_t* gw = baseW + static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + koff;
-      const uint8_t* ga = baseA + static_cast<uint32_t>(min(r, limA)) * rowA + koff;
-      __builtin_amdgcn_global_load_lds(gw, (lds_void_t*)(&lds[stage][0][(it * 32 + wave * 8) * kBK]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(ga, (lds_void_t*)(&lds[stage][1][(it * 32 + wave * 8) * kBK]), 16, 0, 0);
+      const int rb = it * 32 + wave * 8;
+      __builtin_amdgcn_global_load_lds(baseW + offW[it] + koff, (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(baseA + offA[it] + koff, (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
     }
   };
 
-  issue(0, 0);
-  for (int kt = 0; kt < KB; ++kt) {
-    const int stage = kt & 1;
-    if (kt % kScaleWin == 0) {
-      __syncthreads();                 // everyone is done with the previous window
-      const int n = min(kScaleWin, KB - kt);
-      if ((KB & 3) == 0) {
-        for (int s4 = 0; s4 < n; s4 += 4) {
-          const uint32_t vw = *reinterpret_cast<const uint32_t*>(scW + kt + s4);
-          const uint32_t va = *reinterpret_cast<const uint32_t*>(scA + kt + s4);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int sa = (va >> (8 * b)) & 0xFF;
-            sc_dst[(s4 + b) * kScStep] = static_cast<uint8_t>(vw >> (8 * b));
-            sc_dst[(s4 + b) * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(sa) : sa);
-          }
-        }
-      } else {
-        for (int s = 0; s < n; ++s) {
-          const int sa = scA[kt + s];
-          sc_dst[s * kScStep] = scW[kt + s];
-          sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(sa) : sa);
-        }
-      }
-    }
-    // this wave's DMA into `stage` has landed; after the barrier everyone's
-    // has, and everyone is done reading the other stage (step kt-1)
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // fragment reads: row wn*128 + 32*i + lane%32 (W) / wt*128 + 32*j + lane%32
+  // (A); for the 64-K half h, lane group q = lane/32 takes logical chunks
+  // 4h + q and 4h + q + 2
+  const int r32 = lane & 31;
+  const int q2 = lane >> 5;
+  const int rdW = (wn * 128 + r32) * kBK;
+  const int rdA = kOpBytes + (wt * 128 + r32) * kBK;
+  const int sz = swz8(r32);
+  const int ch00 = (q2 ^ sz) << 4, ch01 = ((q2 + 2) ^ sz) << 4;        // half 0
+  const int ch10 = ((4 + q2) ^ sz) << 4, ch11 = ((6 + q2) ^ sz) << 4;  // half 1
 
-    // all operands of this step into registers first ...
-    const int ks = kt % kScaleWin;
-    const uint2 swv = *reinterpret_cast<const uint2*>(&lds_sc[ks][0][wn][r16][0]);
-    const uint2 sav = *reinterpret_cast<const uint2*>(&lds_sc[ks][1][wt][r16][0]);
-    v8i fa[8], fw[8];
+  v8i fw[2][4], fa[2][4];
+  auto read_half = [&](const uint8_t* buf, int c0, int c1, v8i (&w)[4], v8i (&a)[4]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint8_t* q = &lds[stage][1][rdA + j * 16 * kBK];
-      fa[j] = make_v8i(*reinterpret_cast<const uint4*>(q + ch0), *reinterpret_cast<const uint4*>(q + ch1));
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* qw = buf + rdW + i * 32 * kBK;
+      const uint8_t* qa = buf + rdA + i * 32 * kBK;
+      w[i] = make_v8i(*reinterpret_cast<const uint4*>(qw + c0), *reinterpret_cast<const uint4*>(qw + c1));
+      a[i] = make_v8i(*reinterpret_cast<const uint4*>(qa + c0), *reinterpret_cast<const uint4*>(qa + c1));
     }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint8_t* q = &lds[stage][0][rdW + i * 16 * kBK];
-      fw[i] = make_v8i(*reinterpret_cast<const uint4*>(q + ch0), *reinterpret_cast<const uint4*>(q + ch1));
+  };
+
+  // scale staging: thread tid owns W row tid and A row tid
+  const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
+  const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * KB;
+  uint8_t* sc_dst = &lds_sc[0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
+  constexpr int kScStep = 2 * 2 * 32 * 4;
+  constexpr int kScOp = 2 * 32 * 4;
+  auto stage_scales = [&](int first) {
+    const int n = min(kScaleWin, KB - first);
+    for (int s = 0; s < n; ++s) {
+      const int sa = scA[first + s];
+      sc_dst[s * kScStep] = scW[first + s];
+      sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(sa) : sa);
     }
-    // ... then the next step's DMA (after the reads in program order, so the
-    // compiler has no LDS write-after-read hazard to wait for) ...
-    if (kt + 1 < KB) issue(kt + 1, stage ^ 1);
-    // ... then the 64 MFMAs while it flies
+  };
+
+  v16f acc[4][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int sw_i = static_cast<int>(((i < 4 ? swv.x : swv.y) >> (8 * (i & 3))) & 0xFF);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int sa_j = static_cast<int>(((j < 4 ? sav.x : sav.y) >> (8 * (j & 3))) & 0xFF);
-        acc[i][j] = mfma_scaled(fw[i], fa[j], acc[i][j], sw_i, sa_j);
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int sw_i = static_cast<int>((swv >> (8 * i)) & 0xFF);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int sa_j = static_cast<int>((sav >> (8 * j)) & 0xFF);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[i], a[j], acc[i][j], kFmtFp8, kFmtFp8, 0,
+                                                                   sw_i, 0, sa_j);
       }
     }
+  };
+
+  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
+  // lgkmcnt 11:8).  The builtin, unlike inline asm, is seen by the compiler's
+  // own wait insertion, so it does not add a second, later drain.
+  constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
+  constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
+  constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
+
+  // One stage.  On entry stage kb's DMA may still be in flight together with
+  // stage kb+1's (16 instructions); the buffer `cur` holds stage kb.
+  //   wait for stage kb, barrier; read its first 64-K half and run those MFMAs
+  //   while reading its second half; wait for the reads, barrier -- now no
+  //   wave reads `cur` any more -- and refill it with stage kb+2 while the
+  //   second half's MFMAs run.  Each stage's DMA thus has 1.5 stages to land,
+  //   and up to two stages stream at once through 128 KiB of LDS.
+  auto stage = [&](uint8_t* cur, int kb) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitNewest16);
+    __builtin_amdgcn_s_barrier();
+    int ks = kb + kb0;
+    ks -= ks >= KB ? KB : 0;
+    ks &= kScaleWin - 1;
+    const uint32_t swv = *reinterpret_cast<const uint32_t*>(&lds_sc[ks][0][wn][r32][0]);
+    const uint32_t sav = *reinterpret_cast<const uint32_t*>(&lds_sc[ks][1][wt][r32][0]);
+    read_half(cur, ch00, ch01, fw[0], fa[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma_half(fw[0], fa[0], swv, sav);
+    read_half(cur, ch10, ch11, fw[1], fa[1]);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    __builtin_amdgcn_s_barrier();
+    issue(cur, kb + 2);
+    mma_half(fw[1], fa[1], swv, sav);
+    // the MFMAs are pure, so without a use here the compiler would sink them
+    // below the next stage's waits
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  issue(st0, 0);
+  issue(st1, 1);
+  auto window = [&](int kb) {                 // scales of the window starting at stage kb
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    __builtin_amdgcn_s_barrier();             // everyone is done with the previous window
+    stage_scales(kb0 == 0 ? kb : 0);          // rotated K fits one window, staged once
+  };
+  int kb = 0;
+  for (; kb + 2 <= KB; kb += 2) {
+    if (kb % kScaleWin == 0) window(kb);      // kScaleWin is even: windows start on even stages
+    stage(st0, kb);
+    stage(st1, kb + 1);
   }
+  if (kb < KB) {                              // odd number of stages: the last one
+    if (kb % kScaleWin == 0) window(kb);
+    stage(st0, kb);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);      // no DMA outlives the workgroup
 
-  // epilogue: lane holds out[t][n..n+3] for t = col, n = 4*(lane/16) + r
+  // epilogue: lane holds out[t][n] for t = t0 + wt*128 + 32j + lane%32 and
+  // n = n0 + wn*128 + 32i + 8*(r/4) + 4*(lane/32) + r%4 (32x32 accumulator
+  // layout): four consecutive n per 4 registers -> one 8-byte store
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int t = t0 + wt * 128 + j * 16 + r16;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wt * 128 + j * 32 + r32;
     if (t >= p.T) continue;
     uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int n = n0 + wn * 128 + i * 16 + (lane >> 4) * 4;
-      if (n < p.N) *reinterpret_cast<uint2*>(orow + n) = pack4_bf16(acc[i][j]);
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int n = n0 + wn * 128 + i * 32 + r4 * 8 + q2 * 4;
+        if (n < p.N) {
+          const v16f& c = acc[i][j];
+          *reinterpret_cast<uint2*>(orow + n) =
+              make_uint2(pack_bf16x2(c[4 * r4], c[4 * r4 + 1]), pack_bf16x2(c[4 * r4 + 2], c[4 * r4 + 3]));
+        }
+      }
     }
   }
 }

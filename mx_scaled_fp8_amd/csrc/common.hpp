@@ -67,16 +67,13 @@ __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 dv) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float32 -> BF16 bits, round to nearest even on the bit pattern; NaN stays a
-// quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
+// Two floats -> packed BF16 (low = lo), round to nearest even, NaN stays NaN:
+// v_cvt_pk_bf16_f32 (checked bit-exact against integer RNE on 2^20 random
+// FP32 patterns).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  const v2bf_t r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Scale exponent of a group from the BF16 pattern of its amax (sign cleared):

@@ -6,19 +6,27 @@
 // flavour (OCP, or FNUZ capped at 224) follows "[ROCm][DSv4] Functional fixes
 // for DeepSeek V4 on MI300X/MI325X", Purpose.
 //
-// Memory-bound design: every lane owns 8 consecutive BF16 (one 16-byte load);
-// a quantisation group of 128 is 16 consecutive lanes = one DPP row, so its
-// amax is reduced with four row rotations and no LDS; the scale exponent is
-// computed with integer ops on the BF16 bits of the amax; the codes come from
-// the hardware OCP converter (round to nearest even) on r * 2^-e, which is
-// exact because |r * 2^-e| <= 448; each lane stores 8 packed codes (8 bytes).
-// The rotation is fp32 with separately rounded products and sums (this file is
-// built with -ffp-contract=off), then rounded to BF16 before the amax.
+// Design (HBM-bound pass, 3 + 1/128 bytes per element):
+//  * every lane owns 8 consecutive BF16 (one 16-byte load, one 8-byte store);
+//    a group of 128 is 16 consecutive lanes = one DPP row, so its amax is four
+//    row rotations of a packed-u16 max over the BF16 magnitudes, no LDS;
+//  * the scale exponent is integer arithmetic on the BF16 bits of the amax;
+//  * codes come from v_cvt_scalef32_pk_fp8_bf16, which converts two BF16
+//    divided by an E8M0 scale to OCP e4m3 with round-to-nearest-even (checked
+//    against the oracle on every BF16 pattern and scale 2^-127 .. 2^120); the
+//    scale operand is built from its bits, byte << 23, so 2^-127 is exact;
+//  * the rotation is fp32 with separately rounded products and sums (this
+//    file is built with -ffp-contract=off), rounded to BF16 with
+//    v_cvt_pk_bf16_f32 (nearest even) before the amax.
 #include "common.hpp"
 
 namespace mx {
 
 namespace {
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;                       // chunks of 8 elements per lane
@@ -33,6 +41,8 @@ struct QuantArgs {
   uint32_t total_chunks;      // T * L / 8 (this launch)
   DivU32 row_div;             // chunks per row = L / 8
   DivU32 head_div;            // chunks per head = D / 8
+  int32_t row_shift;          // log2(L / 8) when a power of two, else -1
+  int32_t head_shift;         // log2(D / 8) when a power of two, else -1
   uint32_t rope_chunk0;       // (D - R) / 8: first rotated chunk of a head
   uint32_t half_pairs;        // R / 2
   uint2* q;                   // [T, L] codes as 8-byte chunks
@@ -60,6 +70,25 @@ __device__ __forceinline__ uint32_t group_max(uint32_t m) {
   return m;
 }
 
+__device__ __forceinline__ uint32_t div_or_shift(uint32_t n, DivU32 d, int shift) {
+  return shift >= 0 ? (n >> shift) : div_u32(n, d);
+}
+
+// Largest BF16 magnitude pattern of the 8 values in v (packed u16 max).
+__device__ __forceinline__ uint32_t amax_bits8(const uint4 v) {
+  const v2u16 a = __builtin_bit_cast(v2u16, v.x & 0x7FFF7FFFu);
+  const v2u16 b = __builtin_bit_cast(v2u16, v.y & 0x7FFF7FFFu);
+  const v2u16 c = __builtin_bit_cast(v2u16, v.z & 0x7FFF7FFFu);
+  const v2u16 d = __builtin_bit_cast(v2u16, v.w & 0x7FFF7FFFu);
+  const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1]));
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const v2bf r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // (x, y) -> (x*c + y*s, y*c - x*s), every operation rounded to fp32.
 __device__ __forceinline__ void inv_rotate(float x, float y, float c, float s, float& xr, float& yr) {
   const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
@@ -67,21 +96,10 @@ __device__ __forceinline__ void inv_rotate(float x, float y, float c, float s, f
   yr = yc - xs;
 }
 
-__device__ __forceinline__ uint32_t amax_bits8(const uint4 v) {
-  const uint32_t a = v.x & 0x7FFF7FFFu, b = v.y & 0x7FFF7FFFu, c = v.z & 0x7FFF7FFFu, d = v.w & 0x7FFF7FFFu;
-  const uint32_t m0 = max(max(a & 0xFFFFu, a >> 16), max(b & 0xFFFFu, b >> 16));
-  const uint32_t m1 = max(max(c & 0xFFFFu, c >> 16), max(d & 0xFFFFu, d >> 16));
-  return max(m0, m1);
-}
-
-// Rotates the chunk `v` (8 BF16) in place if it lies in a rotated slice.
-// Returns false if the token's position is out of range.
+// Rotates the chunk `v` (8 BF16) in place; `j` is its dim offset inside the
+// rotated slice of a head, `c` its chunk index, `p` the token position.
 template <int STYLE>
-__device__ __forceinline__ bool rope_chunk(const QuantArgs& a, uint32_t c, uint32_t row, uint32_t hchunk,
-                                           int64_t p, uint4& v) {
-  if (hchunk < a.rope_chunk0) return true;
-  if (p < 0 || p >= a.max_pos) return false;
-  const uint32_t j = (hchunk - a.rope_chunk0) * 8;   // dim offset inside the rotated slice
+__device__ __forceinline__ void rope_chunk(const QuantArgs& a, uint32_t c, uint32_t j, int64_t p, uint4& v) {
   const uint16_t* crow = a.cos + p * a.half_pairs;
   const uint16_t* srow = a.sin + p * a.half_pairs;
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -96,10 +114,10 @@ __device__ __forceinline__ bool rope_chunk(const QuantArgs& a, uint32_t c, uint3
     for (int k = 0; k < 4; ++k) {
       float xr, yr;
       inv_rotate(bf16_lo(w[k]), bf16_hi(w[k]), bf16_lo(cw[k]), bf16_lo(sw[k]), xr, yr);
-      w[k] = pack_bf16x2(xr, yr);
+      w[k] = pk_bf16(xr, yr);
     }
   } else {
-    // split halves: this chunk holds one component of pairs i..i+7, the
+    // split halves: this chunk holds one component of pairs i0..i0+7, the
     // partner chunk half_pairs/8 chunks away holds the other
     const bool first = j < a.half_pairs;
     const uint32_t i0 = first ? j : j - a.half_pairs;
@@ -120,20 +138,32 @@ __device__ __forceinline__ bool rope_chunk(const QuantArgs& a, uint32_t c, uint3
       if (first) {
         inv_rotate(own0, oth0, c0, s0, r0x, r0y);
         inv_rotate(own1, oth1, c1, s1, r1x, r1y);
-        w[k] = pack_bf16x2(r0x, r1x);
+        w[k] = pk_bf16(r0x, r1x);
       } else {
         inv_rotate(oth0, own0, c0, s0, r0x, r0y);
         inv_rotate(oth1, own1, c1, s1, r1x, r1y);
-        w[k] = pack_bf16x2(r0y, r1y);
+        w[k] = pk_bf16(r0y, r1y);
       }
     }
   }
   v = make_uint4(w[0], w[1], w[2], w[3]);
-  return true;
 }
 
-// Codes of 8 BF16 values scaled by 2^sh (exact), OCP rounding.
-__device__ __forceinline__ uint2 encode8(const uint4 v, int sh) {
+// OCP codes of the 8 BF16 values of v divided by 2^e: `sbits` is the E8M0
+// byte of 2^e placed in an FP32 exponent field (the converter reads the scale
+// that way).
+__device__ __forceinline__ uint2 encode8(const uint4 v, float sbits) {
+  v2s lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.x), sbits, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.y), sbits, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(v2bf, v.z), sbits, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(v2bf, v.w), sbits, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// Same codes through an exact FP32 rescale, for the one case the E8M0 scale
+// operand cannot express (FNUZ with e = -127 needs a divisor of 2^-128).
+__device__ __forceinline__ uint2 encode8_ldexp(const uint4 v, int sh) {
   int lo = 0, hi = 0;
   lo = cvt_fp8x2<false>(ldexpf(bf16_lo(v.x), sh), ldexpf(bf16_hi(v.x), sh), lo);
   lo = cvt_fp8x2<true>(ldexpf(bf16_lo(v.y), sh), ldexpf(bf16_hi(v.y), sh), lo);
@@ -142,42 +172,70 @@ __device__ __forceinline__ uint2 encode8(const uint4 v, int sh) {
   return make_uint2(static_cast<uint32_t>(lo), static_cast<uint32_t>(hi));
 }
 
+// Lane mapping: a wave is 4 DPP rows of 16 lanes; row r of wave w walks one
+// segment of 64 consecutive chunks (4 groups of 128), chunk u*16 + lane%16 at
+// unroll step u.  With 512-wide heads a segment is one head, so all its
+// rotated chunks (the last 8) fall in step u = 3 and the rotation code runs
+// in one step of four.
 template <int GROUP, int FMT, int STYLE, bool ROPE>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   constexpr int kLanesPerGroup = GROUP / 8;
   constexpr int EM = FMT == MX_FP8_E4M3_OCP ? 8 : 7;
-  const uint32_t base = blockIdx.x * kChunksPerBlock + threadIdx.x;
+  const uint32_t seg = blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
+  const uint32_t base = seg * 64 + (threadIdx.x & 15);
   uint4 v[kUnroll];
   uint32_t cidx[kUnroll];
   // issue all loads first; out-of-range chunks re-read the last valid chunk so
-  // that every lane takes part in the group reductions
+  // that every lane takes part in the group reductions (a group is either all
+  // in range or all out)
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t c = base + u * kThreads;
+    const uint32_t c = base + u * 16;
     cidx[u] = c < a.total_chunks ? c : a.total_chunks - 1;
     v[u] = a.x[cidx[u]];
+  }
+  uint32_t row = 0, cin0 = 0;
+  int64_t p = 0;
+  bool ok = true;
+  if constexpr (ROPE) {
+    row = div_or_shift(cidx[0], a.row_div, a.row_shift);
+    cin0 = cidx[0] - row * a.row_div.d;
+    p = a.pos[row];
+    ok = p >= 0 && p < a.max_pos;
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t c = cidx[u];
-    bool ok = true;
     if constexpr (ROPE) {
-      const uint32_t row = div_u32(c, a.row_div);
-      const uint32_t cin = c - row * a.row_div.d;
-      const uint32_t hrow = div_u32(cin, a.head_div);
+      uint32_t cin = cin0 + u * 16;
+      if (a.row_shift < 0 || cin >= a.row_div.d || c != cidx[0] + u * 16) {
+        // the segment crosses a row (rows not a multiple of 512 elements) or
+        // this chunk was clamped: locate it from scratch
+        const uint32_t r = div_or_shift(c, a.row_div, a.row_shift);
+        cin = c - r * a.row_div.d;
+        if (r != row) {
+          const int64_t pr = a.pos[r];
+          ok = pr >= 0 && pr < a.max_pos;
+          p = pr;
+          row = r;
+        }
+      }
+      const uint32_t hrow = div_or_shift(cin, a.head_div, a.head_shift);
       const uint32_t hchunk = cin - hrow * a.head_div.d;
-      const int64_t p = a.pos[row];
-      if (p < 0 || p >= a.max_pos) ok = false;
-      else ok = rope_chunk<STYLE>(a, c, row, hchunk, p, v[u]);
+      if (ok && hchunk >= a.rope_chunk0) rope_chunk<STYLE>(a, c, (hchunk - a.rope_chunk0) * 8, p, v[u]);
     }
     uint32_t m = amax_bits8(v[u]);
-    if (!ok) m = 0x7F80u;                 // mark the whole group bad
+    if (!ok) m = 0x7F80u;                 // position outside the table: mark the group bad
     m = group_max<GROUP>(m);
     const bool finite = m < 0x7F80u;
     const int e = e8m0_exponent<EM>(finite ? m : 0);
     // FNUZ code of r*2^-e = OCP code of r*2^-(e-1)
-    const int sh = FMT == MX_FP8_E4M3_OCP ? -e : 1 - e;
-    uint2 codes = encode8(v[u], sh);
+    const int ecvt = FMT == MX_FP8_E4M3_OCP ? e : e - 1;
+    uint2 codes;
+    if (FMT == MX_FP8_E4M3_FNUZ && ecvt < -127)
+      codes = encode8_ldexp(v[u], -ecvt);
+    else
+      codes = encode8(v[u], __uint_as_float(static_cast<uint32_t>(ecvt + 127) << 23));
     if constexpr (FMT == MX_FP8_E4M3_FNUZ) {
       codes.x = ocp_negzero_to_fnuz(codes.x);
       codes.y = ocp_negzero_to_fnuz(codes.y);
@@ -186,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       const uint32_t nan4 = FMT == MX_FP8_E4M3_OCP ? 0x7F7F7F7Fu : 0x80808080u;
       codes = make_uint2(nan4, nan4);
     }
-    const uint32_t craw = base + u * kThreads;
+    const uint32_t craw = base + u * 16;
     if (craw < a.total_chunks) {
       a.q[craw] = codes;
       if ((threadIdx.x & (kLanesPerGroup - 1)) == 0)
@@ -203,6 +261,13 @@ void launch_style(const QuantArgs& a, bool rope, int style, uint32_t blocks, hip
     quant_kernel<GROUP, FMT, MX_ROPE_INTERLEAVED, true><<<blocks, kThreads, 0, s>>>(a);
   else
     quant_kernel<GROUP, FMT, MX_ROPE_NEOX, true><<<blocks, kThreads, 0, s>>>(a);
+}
+
+int log2_if_pow2(uint32_t v) {
+  if (v == 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1u << s) != v) ++s;
+  return s;
 }
 
 }  // namespace
@@ -227,6 +292,8 @@ mx_status launch_quant(const void* x, const int64_t* positions, const void* cos,
     a.total_chunks = static_cast<uint32_t>(rows * chunks_per_row);
     a.row_div = make_div(static_cast<uint32_t>(chunks_per_row));
     a.head_div = make_div(static_cast<uint32_t>(D / 8));
+    a.row_shift = log2_if_pow2(static_cast<uint32_t>(chunks_per_row));
+    a.head_shift = log2_if_pow2(static_cast<uint32_t>(D / 8));
     a.rope_chunk0 = static_cast<uint32_t>((D - rope_dim) / 8);
     a.half_pairs = static_cast<uint32_t>(rope_dim / 2);
     a.q = reinterpret_cast<uint2*>(q + r0 * L);
