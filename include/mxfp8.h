@@ -139,8 +139,7 @@ mx_status mx_inv_rope_group_quant(const void* x, const int64_t* positions,
  * w_scale  device u8 [G, N, K/128].
  * out      device BF16 [T, G, N].
  * Requires: T >= 0 (0 is a no-op), G >= 1, N >= 1 with N % 16 == 0, K >= 128
- * with K % 128 == 0, a/w 16-byte aligned, a_scale/w_scale 4-byte aligned,
- * out 8-byte aligned.
+ * with K % 128 == 0, a, w and out 16-byte aligned.
  */
 mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t a_fmt,
                               const uint8_t* w, const uint8_t* w_scale, void* out,

@@ -197,7 +197,7 @@ mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t 
   if (T == 0) { clear_error(); return MX_OK; }
   MX_CHECK(a && a_scale && w && w_scale && out, "%s: null tensor pointer", fn);
   MX_CHECK(aligned(a, 16) && aligned(w, 16), "%s: a and w must be 16-byte aligned", fn);
-  MX_CHECK(aligned(out, 8), "%s: out must be 8-byte aligned", fn);
+  MX_CHECK(aligned(out, 16), "%s: out must be 16-byte aligned", fn);
   MX_PREAMBLE();
   const mx_status st = launch_bmm(a, a_scale, a_fmt, w, w_scale, out, T, G, N, K, static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();

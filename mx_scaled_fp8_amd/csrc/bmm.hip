@@ -125,10 +125,13 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   const int wave = tid >> 6;
   const int wn = wave & 1, wt = wave >> 1;     // wave's 128x128 sub-tile
   const int KB = p.K / kBK;                    // stages
-  // each tile starts its K loop at a different stage, so that the workgroups
-  // sharing an XCD do not all stream the same K offset at once (when the
-  // whole K fits one scale window; otherwise from 0)
-  const int kb0 = KB <= kScaleWin ? work % KB : 0;
+  // Tiles start their K loop at stage (tt + nt) mod KB: the workgroups that
+  // share an XCD spread over a few neighbouring K offsets (so their rows do
+  // not all hit one memory channel at once), while the tiles that share an
+  // activation panel (same tt) or a weight tile (same nt) stay within a few
+  // stages of each other and still find the shared rows in L2.  Rotation
+  // needs every scale in one window, so it is used when K fits one.
+  const int kb0 = KB <= kScaleWin ? (tt + nt) % KB : 0;
   const uint32_t rowA = static_cast<uint32_t>(p.G) * p.K;   // activation row stride
 
   // LDS-DMA sources: wave `wave` fills rows it*32 + wave*8 + lane/8 (it =
@@ -146,8 +149,8 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     offW[it] = static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + dma_chunk;
     offA[it] = static_cast<uint32_t>(min(r, limA)) * rowA + dma_chunk;
   }
-  auto issue = [&](uint8_t* buf, int kb) {   // kb >= KB re-reads the last stage (harmless)
-    int kr = min(kb, KB - 1) + kb0;
+  auto issue = [&](uint8_t* buf, int kb) {   // requires kb < KB
+    int kr = kb + kb0;
     kr -= kr >= KB ? KB : 0;
     const uint32_t koff = static_cast<uint32_t>(kr) * kBK;
 #pragma unroll
@@ -180,19 +183,42 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     }
   };
 
-  // scale staging: thread tid owns W row tid and A row tid
+  // scale staging: thread tid owns W row tid and A row tid; slot s of the
+  // window that starts at loop stage `first` holds stage (first + s + kb0) mod KB
   const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
   const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * KB;
   uint8_t* sc_dst = &lds_sc[0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
   constexpr int kScStep = 2 * 2 * 32 * 4;
   constexpr int kScOp = 2 * 32 * 4;
-  auto stage_scales = [&](int first) {
+  auto stage_scales_serial = [&](int first) {   // few registers: for the loop (K > one window)
     const int n = min(kScaleWin, KB - first);
     for (int s = 0; s < n; ++s) {
-      const int sa = scA[first + s];
-      sc_dst[s * kScStep] = scW[first + s];
+      const int ks = first + s;                  // kb0 == 0 whenever windows change in the loop
+      const int sa = scA[ks];
+      sc_dst[s * kScStep] = scW[ks];
       sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(sa) : sa);
     }
+  };
+  auto stage_scales = [&](int first) {          // all loads first, then the LDS writes
+    uint8_t bw[kScaleWin], ba[kScaleWin];
+#pragma unroll
+    for (int s = 0; s < kScaleWin; ++s) {
+      int ks = first + s + kb0;                  // kb0 > 0 only when first == 0 and KB <= kScaleWin
+      ks -= ks >= KB ? KB : 0;
+      ks = min(ks, KB - 1);                      // slots past the last stage read a valid byte
+      bw[s] = scW[ks];
+      ba[s] = scA[ks];
+    }
+#pragma unroll
+    for (int s = 0; s < kScaleWin; ++s) {        // slots past the last stage are never read
+      sc_dst[s * kScStep] = bw[s];
+      sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(ba[s]) : ba[s]);
+    }
+  };
+  auto read_scales = [&](int kb, uint32_t& swv, uint32_t& sav) {
+    const int s = kb & (kScaleWin - 1);
+    swv = *reinterpret_cast<const uint32_t*>(&lds_sc[s][0][wn][r32][0]);
+    sav = *reinterpret_cast<const uint32_t*>(&lds_sc[s][1][wt][r32][0]);
   };
 
   v16f acc[4][4];
@@ -215,6 +241,14 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
       }
     }
   };
+  // the MFMAs are pure, so without a use the compiler would sink them below
+  // the following waits and barrier
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+  };
 
   // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
   // lgkmcnt 11:8).  The builtin, unlike inline asm, is seen by the compiler's
@@ -223,23 +257,22 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
   constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
 
-  // One stage.  On entry stage kb's DMA may still be in flight together with
-  // stage kb+1's (16 instructions); the buffer `cur` holds stage kb.
-  //   wait for stage kb, barrier; read its first 64-K half and run those MFMAs
-  //   while reading its second half; wait for the reads, barrier -- now no
-  //   wave reads `cur` any more -- and refill it with stage kb+2 while the
-  //   second half's MFMAs run.  Each stage's DMA thus has 1.5 stages to land,
-  //   and up to two stages stream at once through 128 KiB of LDS.
-  auto stage = [&](uint8_t* cur, int kb) {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitNewest16);
-    __builtin_amdgcn_s_barrier();
-    int ks = kb + kb0;
-    ks -= ks >= KB ? KB : 0;
-    ks &= kScaleWin - 1;
-    const uint32_t swv = *reinterpret_cast<const uint32_t*>(&lds_sc[ks][0][wn][r32][0]);
-    const uint32_t sav = *reinterpret_cast<const uint32_t*>(&lds_sc[ks][1][wt][r32][0]);
-    read_half(cur, ch00, ch01, fw[0], fa[0]);
+  // One stage, one barrier, in two parts.  On entry to front(kb) the first
+  // 64-K half of stage kb is in registers (fw[0], fa[0]) with its scales,
+  // `cur` holds stage kb and this wave's DMA of stage kb+1 into `nxt` may be
+  // in flight.
+  //   front: MFMAs of half 0 while reading half 1 of `cur`; wait for this
+  //          wave's reads and DMA, barrier -- now stage kb+1 is in `nxt` and
+  //          no wave reads `cur` any more;
+  //   back:  refill `cur` with stage kb+2 by DMA, then the MFMAs of half 1
+  //          while reading half 0 of stage kb+1 (and its scales) from `nxt`.
+  // Fragment reads always overlap MFMAs and each DMA has one stage to land.
+  // The loop runs back..front, so at its head (just after a barrier that
+  // followed a full wait) no DMA is pending: the compiler then sees, in
+  // straight-line code, that the reads of one buffer never alias the DMA into
+  // the other and adds no wait of its own.
+  uint32_t swv, sav;
+  auto front = [&](const uint8_t* cur, int kb, bool new_window) {
     __builtin_amdgcn_sched_barrier(0);
     mma_half(fw[0], fa[0], swv, sav);
     read_half(cur, ch10, ch11, fw[1], fa[1]);
@@ -248,62 +281,101 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     __builtin_amdgcn_s_barrier();
-    issue(cur, kb + 2);
+    if (new_window) {                        // K spans several windows: restage the scales
+      stage_scales_serial(kb + 1);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+      __builtin_amdgcn_s_barrier();
+    }
+  };
+  auto back = [&](uint8_t* cur, const uint8_t* nxt, int kb, bool dma) {
+    if (dma) issue(cur, kb + 2);
+    uint32_t swv1, sav1;
+    read_scales(kb + 1, swv1, sav1);
     mma_half(fw[1], fa[1], swv, sav);
-    // the MFMAs are pure, so without a use here the compiler would sink them
-    // below the next stage's waits
+    read_half(nxt, ch00, ch01, fw[0], fa[0]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+    for (int k = 0; k < 16; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
+    swv = swv1;
+    sav = sav1;
+  };
+  auto window_at = [&](int kb) {             // front(kb) restages scales for stage kb+1
+    return KB > kScaleWin && (kb + 1) % kScaleWin == 0 && kb + 1 < KB;
   };
 
+  // prologue: scales of the first window, stages 0 and 1 in flight, half 0 of
+  // stage 0 in registers
   issue(st0, 0);
-  issue(st1, 1);
-  auto window = [&](int kb) {                 // scales of the window starting at stage kb
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-    __builtin_amdgcn_s_barrier();             // everyone is done with the previous window
-    stage_scales(kb0 == 0 ? kb : 0);          // rotated K fits one window, staged once
-  };
-  int kb = 0;
-  for (; kb + 2 <= KB; kb += 2) {
-    if (kb % kScaleWin == 0) window(kb);      // kScaleWin is even: windows start on even stages
-    stage(st0, kb);
-    stage(st1, kb + 1);
-  }
-  if (kb < KB) {                              // odd number of stages: the last one
-    if (kb % kScaleWin == 0) window(kb);
-    stage(st0, kb);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitAll);      // no DMA outlives the workgroup
+  stage_scales(0);                              // its loads complete after stage 0's DMA
+  issue(st1, min(1, KB - 1));                   // (KB == 1: a harmless second copy of stage 0)
+  __builtin_amdgcn_s_waitcnt(kWaitNewest16);
+  __builtin_amdgcn_s_barrier();
+  read_scales(0, swv, sav);
+  read_half(st0, ch00, ch01, fw[0], fa[0]);
 
-  // epilogue: lane holds out[t][n] for t = t0 + wt*128 + 32j + lane%32 and
-  // n = n0 + wn*128 + 32i + 8*(r/4) + 4*(lane/32) + r%4 (32x32 accumulator
-  // layout): four consecutive n per 4 registers -> one 8-byte store
+  front(st0, 0, window_at(0));
+  int kb = 0;
+  for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
+    back(st0, st1, kb, true);
+    front(st1, kb + 1, window_at(kb + 1));
+    back(st1, st0, kb + 1, kb + 3 < KB);
+    front(st0, kb + 2, window_at(kb + 2));
+  }
+  if (kb + 1 < KB) {                            // two stages left, the first begun
+    back(st0, st1, kb, false);
+    front(st1, kb + 1, false);
+  }
+  mma_half(fw[1], fa[1], swv, sav);             // second half of the last stage
+  __builtin_amdgcn_s_waitcnt(kWaitAll);         // no DMA or LDS read outlives the loop
+
+  // Epilogue through LDS, so that every global store writes whole rows.
+  // Lane holds tile element (t, n) for t = wt*128 + 32j + lane%32 and n =
+  // wn*128 + 32i + 8*(r/4) + 4*(lane/32) + r%4 (32x32 accumulator layout):
+  // four consecutive n per four registers.  The waves with wt = 0 write tile
+  // rows 0..127 into st0, those with wt = 1 rows 128..255 into st1; a row is
+  // 512 B (256 n), and its 16-byte chunk c sits at physical chunk c ^ (row % 32),
+  // which keeps both the 8-byte writes and the 16-byte row reads free of bank
+  // conflicts.  Then wave w stores tile rows 64w .. 64w+63, two 512-byte rows
+  // per instruction.
+  __builtin_amdgcn_s_barrier();                  // all fragment reads are done (waited above)
+  {
+    uint8_t* img = wt ? st1 : st0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + wt * 128 + j * 32 + r32;
-    if (t >= p.T) continue;
-    uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
+    for (int j = 0; j < 4; ++j) {
+      const int tl = j * 32 + r32;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int n = n0 + wn * 128 + i * 32 + r4 * 8 + q2 * 4;
-        if (n < p.N) {
-          const v16f& c = acc[i][j];
-          *reinterpret_cast<uint2*>(orow + n) =
-              make_uint2(pack_bf16x2(c[4 * r4], c[4 * r4 + 1]), pack_bf16x2(c[4 * r4 + 2], c[4 * r4 + 3]));
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int c = wn * 16 + i * 4 + r4;
+          const v16f& v = acc[i][j];
+          *reinterpret_cast<uint2*>(img + tl * 512 + ((c ^ (tl & 31)) << 4) + q2 * 8) =
+              make_uint2(pack_bf16x2(v[4 * r4], v[4 * r4 + 1]), pack_bf16x2(v[4 * r4 + 2], v[4 * r4 + 3]));
         }
       }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+  __builtin_amdgcn_s_barrier();
+  {
+    const uint8_t* img = wave < 2 ? st0 : st1;
+    const int c = lane & 31;
+    const int n = n0 + c * 8;
+#pragma unroll 4
+    for (int s = 0; s < 32; ++s) {
+      const int row = (wave & 1) * 64 + 2 * s + q2;
+      const int t = t0 + (wave >> 1) * 128 + row;
+      const uint4 v = *reinterpret_cast<const uint4*>(img + row * 512 + ((c ^ (row & 31)) << 4));
+      if (t < p.T && n < p.N)
+        *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + g) * p.N + n) = v;
     }
   }
 }
