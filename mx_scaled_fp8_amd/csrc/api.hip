@@ -62,6 +62,14 @@ mx_status launch_status(const char* what) {
   return MX_OK;
 }
 
+static std::atomic<int> g_cus[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  return g_cus[dev].load(std::memory_order_relaxed);
+}
+
 static mx_status probe_device(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return fail(MX_ERR_INVALID_ARG, "mx_probe: device %d out of range", dev);
   int state = g_probe[dev].load(std::memory_order_acquire);
@@ -75,6 +83,7 @@ static mx_status probe_device(int dev) {
     } else {
       std::snprintf(arch, sizeof(arch), "%s", prop.gcnArchName);
       state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+      g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
     }
     g_probe[dev].store(state, std::memory_order_release);
     if (log_enabled()) {

@@ -35,6 +35,7 @@
 //  * small-T (T <= 64, decode and the MXFP8 linear): one workgroup per
 //    (g, 16*NT n) with all T rows; the 4 waves split K and reduce through LDS.
 //    Operands stream straight from global memory (weight-bandwidth bound).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -100,7 +101,18 @@ struct LargeArgs {
   uint16_t* out;         // [T, G, N]
   int T, G, N, K;
   int tiles_t, tiles_n, total_tiles, per_xcd;
+  int wg_per_xcd;        // persistent kernel: resident workgroups per XCD
 };
+
+// One 32x32x64 block-scaled MFMA of the large kernel: W tile I times A tile
+// J.  The scale operands are 4-byte words holding the scales of tiles 0..3;
+// the byte-select operands pick byte I of the W word and byte J of the A word.
+template <int I, int J>
+__device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+                                        uint32_t sav) {
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[I], a[J], acc[I][J], kFmtFp8, kFmtFp8, I,
+                                                             static_cast<int>(swv), J, static_cast<int>(sav));
+}
 
 template <bool A_FNUZ>
 __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
@@ -149,15 +161,17 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     offW[it] = static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + dma_chunk;
     offA[it] = static_cast<uint32_t>(min(r, limA)) * rowA + dma_chunk;
   }
-  auto issue = [&](uint8_t* buf, int kb) {   // requires kb < KB
-    int kr = kb + kb0;
+  auto issue = [&](uint8_t* buf, int kb) {   // kb >= KB re-reads the last stage
+    int kr = min(kb, KB - 1) + kb0;
     kr -= kr >= KB ? KB : 0;
-    const uint32_t koff = static_cast<uint32_t>(kr) * kBK;
+    // uniform base + 32-bit lane offset: the scalar-base addressing form
+    const uint8_t* bW = baseW + static_cast<uint32_t>(kr) * kBK;
+    const uint8_t* bA = baseA + static_cast<uint32_t>(kr) * kBK;
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int rb = it * 32 + wave * 8;
-      __builtin_amdgcn_global_load_lds(baseW + offW[it] + koff, (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(baseA + offA[it] + koff, (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bW + offW[it], (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bA + offA[it], (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
     }
   };
 
@@ -173,50 +187,68 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   const int ch10 = ((4 + q2) ^ sz) << 4, ch11 = ((6 + q2) ^ sz) << 4;  // half 1
 
   v8i fw[2][4], fa[2][4];
+  auto read_frag = [&](const uint8_t* q, int c0, int c1) {
+    return make_v8i(*reinterpret_cast<const uint4*>(q + c0), *reinterpret_cast<const uint4*>(q + c1));
+  };
   auto read_half = [&](const uint8_t* buf, int c0, int c1, v8i (&w)[4], v8i (&a)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint8_t* qw = buf + rdW + i * 32 * kBK;
-      const uint8_t* qa = buf + rdA + i * 32 * kBK;
-      w[i] = make_v8i(*reinterpret_cast<const uint4*>(qw + c0), *reinterpret_cast<const uint4*>(qw + c1));
-      a[i] = make_v8i(*reinterpret_cast<const uint4*>(qa + c0), *reinterpret_cast<const uint4*>(qa + c1));
-    }
+    const uint8_t* qw = buf + rdW;
+    const uint8_t* qa = buf + rdA;
+    w[0] = read_frag(qw, c0, c1);
+    a[0] = read_frag(qa, c0, c1);
+    a[1] = read_frag(qa + 32 * kBK, c0, c1);
+    w[1] = read_frag(qw + 32 * kBK, c0, c1);
+    a[2] = read_frag(qa + 64 * kBK, c0, c1);
+    w[2] = read_frag(qw + 64 * kBK, c0, c1);
+    a[3] = read_frag(qa + 96 * kBK, c0, c1);
+    w[3] = read_frag(qw + 96 * kBK, c0, c1);
   };
 
-  // scale staging: thread tid owns W row tid and A row tid; slot s of the
-  // window that starts at loop stage `first` holds stage (first + s + kb0) mod KB
+  // scale staging: thread tid owns W row tid and A row tid.  LDS slot s of
+  // the window holds stage s of the window (the actual stage, not the loop
+  // index: with the rotation, loop stage kb reads slot (kb + kb0) mod KB).
   const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
   const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * KB;
   uint8_t* sc_dst = &lds_sc[0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
   constexpr int kScStep = 2 * 2 * 32 * 4;
   constexpr int kScOp = 2 * 32 * 4;
+  auto put_scales = [&](int s, uint32_t bw, uint32_t ba) {
+    sc_dst[s * kScStep] = static_cast<uint8_t>(bw);
+    sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(static_cast<int>(ba)) : ba);
+  };
   auto stage_scales_serial = [&](int first) {   // few registers: for the loop (K > one window)
     const int n = min(kScaleWin, KB - first);
-    for (int s = 0; s < n; ++s) {
-      const int ks = first + s;                  // kb0 == 0 whenever windows change in the loop
-      const int sa = scA[ks];
-      sc_dst[s * kScStep] = scW[ks];
-      sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(sa) : sa);
-    }
+    for (int s = 0; s < n; ++s) put_scales(s, scW[first + s], scA[first + s]);
   };
-  auto stage_scales = [&](int first) {          // all loads first, then the LDS writes
-    uint8_t bw[kScaleWin], ba[kScaleWin];
+  auto stage_scales_first = [&]() {             // the first window, before the loop
+    if ((KB & 15) == 0 && ((reinterpret_cast<uintptr_t>(scW) | reinterpret_cast<uintptr_t>(scA)) & 15) == 0) {
+      // two 16-byte loads per row instead of 32 byte loads
+      const uint4 w0 = *reinterpret_cast<const uint4*>(scW), a0 = *reinterpret_cast<const uint4*>(scA);
+      uint4 w1 = make_uint4(0, 0, 0, 0), a1 = w1;
+      if (KB >= 32) {
+        w1 = *reinterpret_cast<const uint4*>(scW + 16);
+        a1 = *reinterpret_cast<const uint4*>(scA + 16);
+      }
+      const uint32_t ww[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int s = 0; s < kScaleWin; ++s) {
-      int ks = first + s + kb0;                  // kb0 > 0 only when first == 0 and KB <= kScaleWin
-      ks -= ks >= KB ? KB : 0;
-      ks = min(ks, KB - 1);                      // slots past the last stage read a valid byte
-      bw[s] = scW[ks];
-      ba[s] = scA[ks];
-    }
+      for (int s = 0; s < kScaleWin; ++s)        // slots past the last stage are never read
+        put_scales(s, (ww[s >> 2] >> (8 * (s & 3))) & 0xFF, (aw[s >> 2] >> (8 * (s & 3))) & 0xFF);
+    } else {
+      uint8_t bw[kScaleWin], ba[kScaleWin];      // all loads first, then the LDS writes
 #pragma unroll
-    for (int s = 0; s < kScaleWin; ++s) {        // slots past the last stage are never read
-      sc_dst[s * kScStep] = bw[s];
-      sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(ba[s]) : ba[s]);
+      for (int s = 0; s < kScaleWin; ++s) {
+        const int ks = min(s, KB - 1);           // slots past the last stage read a valid byte
+        bw[s] = scW[ks];
+        ba[s] = scA[ks];
+      }
+#pragma unroll
+      for (int s = 0; s < kScaleWin; ++s) put_scales(s, bw[s], ba[s]);
     }
   };
   auto read_scales = [&](int kb, uint32_t& swv, uint32_t& sav) {
-    const int s = kb & (kScaleWin - 1);
+    int ks = kb + kb0;                           // the stage loop index kb covers
+    ks -= ks >= KB ? KB : 0;
+    const int s = ks & (kScaleWin - 1);
     swv = *reinterpret_cast<const uint32_t*>(&lds_sc[s][0][wn][r32][0]);
     sav = *reinterpret_cast<const uint32_t*>(&lds_sc[s][1][wt][r32][0]);
   };
@@ -229,17 +261,27 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // The 16 MFMAs of a 64-K half, in the order the fragments arrive (read_half
+  // reads w0 a0 a1 w1 a2 w2 a3 w3), so that each MFMA waits only for the
+  // fragments it uses.  The scale operand is the whole 4-byte word; the
+  // instruction's byte select picks tile i's (j's) byte.
   auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int sw_i = static_cast<int>((swv >> (8 * i)) & 0xFF);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int sa_j = static_cast<int>((sav >> (8 * j)) & 0xFF);
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[i], a[j], acc[i][j], kFmtFp8, kFmtFp8, 0,
-                                                                   sw_i, 0, sa_j);
-      }
-    }
+    mfma_ij<0, 0>(acc, w, a, swv, sav);
+    mfma_ij<0, 1>(acc, w, a, swv, sav);
+    mfma_ij<1, 0>(acc, w, a, swv, sav);
+    mfma_ij<1, 1>(acc, w, a, swv, sav);
+    mfma_ij<0, 2>(acc, w, a, swv, sav);
+    mfma_ij<1, 2>(acc, w, a, swv, sav);
+    mfma_ij<2, 0>(acc, w, a, swv, sav);
+    mfma_ij<2, 1>(acc, w, a, swv, sav);
+    mfma_ij<2, 2>(acc, w, a, swv, sav);
+    mfma_ij<0, 3>(acc, w, a, swv, sav);
+    mfma_ij<1, 3>(acc, w, a, swv, sav);
+    mfma_ij<2, 3>(acc, w, a, swv, sav);
+    mfma_ij<3, 0>(acc, w, a, swv, sav);
+    mfma_ij<3, 1>(acc, w, a, swv, sav);
+    mfma_ij<3, 2>(acc, w, a, swv, sav);
+    mfma_ij<3, 3>(acc, w, a, swv, sav);
   };
   // the MFMAs are pure, so without a use the compiler would sink them below
   // the following waits and barrier
@@ -276,11 +318,13 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     mma_half(fw[0], fa[0], swv, sav);
     read_half(cur, ch10, ch11, fw[1], fa[1]);
+    // reads early in the half (two per MFMA), so they land before the half ends
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 8; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -297,10 +341,19 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     read_scales(kb + 1, swv1, sav1);
     mma_half(fw[1], fa[1], swv, sav);
     read_half(nxt, ch00, ch01, fw[0], fa[0]);
+    // one DMA instruction per MFMA: a burst of 16 would stall this wave on the
+    // texture-address unit, which takes the four waves' DMA at about the rate
+    // the MFMAs run; the LDS reads go early (two per MFMA)
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < 9; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // (the first two are the scales)
+    }
+#pragma unroll
+    for (int k = 0; k < 7; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
@@ -314,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   // prologue: scales of the first window, stages 0 and 1 in flight, half 0 of
   // stage 0 in registers
   issue(st0, 0);
-  stage_scales(0);                              // its loads complete after stage 0's DMA
+  stage_scales_first();                         // its loads complete after stage 0's DMA
   issue(st1, min(1, KB - 1));                   // (KB == 1: a harmless second copy of stage 0)
   __builtin_amdgcn_s_waitcnt(kWaitNewest16);
   __builtin_amdgcn_s_barrier();
@@ -323,10 +376,14 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
 
   front(st0, 0, window_at(0));
   int kb = 0;
+  // Both DMAs of the body are unconditional: a conditional one would be
+  // issued as a block ahead of the MFMAs.  With an odd number of stages the
+  // last iteration's second DMA asks for stage KB; issue() clamps it to a
+  // valid stage, and the buffer it fills (st1) is not read again.
   for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
     back(st0, st1, kb, true);
     front(st1, kb + 1, window_at(kb + 1));
-    back(st1, st0, kb + 1, kb + 3 < KB);
+    back(st1, st0, kb + 1, true);
     front(st0, kb + 2, window_at(kb + 2));
   }
   if (kb + 1 < KB) {                            // two stages left, the first begun
@@ -336,48 +393,325 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   mma_half(fw[1], fa[1], swv, sav);             // second half of the last stage
   __builtin_amdgcn_s_waitcnt(kWaitAll);         // no DMA or LDS read outlives the loop
 
-  // Epilogue through LDS, so that every global store writes whole rows.
-  // Lane holds tile element (t, n) for t = wt*128 + 32j + lane%32 and n =
-  // wn*128 + 32i + 8*(r/4) + 4*(lane/32) + r%4 (32x32 accumulator layout):
-  // four consecutive n per four registers.  The waves with wt = 0 write tile
-  // rows 0..127 into st0, those with wt = 1 rows 128..255 into st1; a row is
-  // 512 B (256 n), and its 16-byte chunk c sits at physical chunk c ^ (row % 32),
-  // which keeps both the 8-byte writes and the 16-byte row reads free of bank
-  // conflicts.  Then wave w stores tile rows 64w .. 64w+63, two 512-byte rows
-  // per instruction.
-  __builtin_amdgcn_s_barrier();                  // all fragment reads are done (waited above)
-  {
-    uint8_t* img = wt ? st1 : st0;
+  // Epilogue straight from the accumulators.  Lane holds tile element (t, n)
+  // for t = wt*128 + 32j + lane%32 and n = wn*128 + 32i + 8*(r/4) +
+  // 4*(lane/32) + r%4 (32x32 accumulator layout): four consecutive n per four
+  // registers.  v_permlane32_swap exchanges the register groups r/4 = 2p+1 of
+  // lanes 0..31 with the groups 2p of lanes 32..63, after which lane l < 32
+  // holds n = 16p .. 16p+7 of its token and lane l + 32 n = 16p+8 .. 16p+15:
+  // one 16-byte store each, 32 bytes per token row per instruction.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = j * 32 + r32;
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wt * 128 + j * 32 + r32;
+    uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      const v16f& v = acc[i][j];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int c = wn * 16 + i * 4 + r4;
-          const v16f& v = acc[i][j];
-          *reinterpret_cast<uint2*>(img + tl * 512 + ((c ^ (tl & 31)) << 4) + q2 * 8) =
-              make_uint2(pack_bf16x2(v[4 * r4], v[4 * r4 + 1]), pack_bf16x2(v[4 * r4 + 2], v[4 * r4 + 3]));
-        }
+      for (int pp = 0; pp < 2; ++pp) {
+        const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+        const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const int n = n0 + wn * 128 + i * 32 + pp * 16 + q2 * 8;
+        if (t < p.T && n < p.N)
+          *reinterpret_cast<uint4*>(orow + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-  __builtin_amdgcn_s_barrier();
-  {
-    const uint8_t* img = wave < 2 ? st0 : st1;
-    const int c = lane & 31;
-    const int n = n0 + c * 8;
-#pragma unroll 4
-    for (int s = 0; s < 32; ++s) {
-      const int row = (wave & 1) * 64 + 2 * s + q2;
-      const int t = t0 + (wave >> 1) * 128 + row;
-      const uint4 v = *reinterpret_cast<const uint4*>(img + row * 512 + ((c ^ (row & 31)) << 4));
-      if (t < p.T && n < p.N)
-        *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + g) * p.N + n) = v;
+}
+
+// ------------------------------------------------- persistent large tiles
+//
+// The tiles, stages and fragment pipeline of bmm_large_kernel, with each
+// workgroup resident for the whole GEMM: workgroup (xcd, slot) takes tiles
+// slot, slot + wg_per_xcd, ... of its XCD's range, in the same order as the
+// one-tile-per-workgroup launch.  The next tile's stages 0 and 1 and its
+// scales are fetched during the current tile's last two stages (scales go to
+// the other of two LDS scale buffers), so the stage pipeline runs through
+// tile boundaries and only the epilogue stores sit between two tiles.
+// Requires K / 128 in {16, 32} (an even number of stages, all scales of a
+// tile in one window) and 16-byte aligned scale tensors; other shapes use
+// bmm_large_kernel.
+template <bool A_FNUZ>
+__global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kOpBytes];
+  // two scale buffers (current tile, next tile), each [stage][W|A][wave half][row % 32][tile]
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[2][kScaleWin][2][2][32][4];
+
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wn = wave & 1, wt = wave >> 1;
+  const int KB = p.K / kBK;                    // 16 or 32
+  const uint32_t rowA = static_cast<uint32_t>(p.G) * p.K;
+
+  // tile r of this workgroup; false past the end of its XCD's range
+  auto tile_at = [&](int r, int& g, int& t0, int& n0, int& kb0) {
+    const int li = slot + r * p.wg_per_xcd;
+    const int work = xcd * p.per_xcd + li;
+    if (li >= p.per_xcd || work >= p.total_tiles) return false;
+    const int nt = work % p.tiles_n;
+    const int tt = (work / p.tiles_n) % p.tiles_t;
+    g = work / (p.tiles_n * p.tiles_t);
+    t0 = tt * kLT;
+    n0 = nt * kLN;
+    kb0 = (tt + nt) % KB;                      // K rotation, as in bmm_large_kernel
+    return true;
+  };
+
+  // ---- DMA of one tile's stages (the tile whose stages are being fetched)
+  const int dma_row = wave * 8 + (lane >> 3);
+  const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz8(dma_row)) * 16;
+  uint32_t offW[8], offA[8];
+  const uint8_t* dW;
+  const uint8_t* dA;
+  int dkb0;
+  auto set_dma_tile = [&](int g, int t0, int n0, int kb0) {
+    dW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
+    dA = p.a + static_cast<size_t>(t0) * rowA + static_cast<size_t>(g) * p.K;
+    dkb0 = kb0;
+    const int limW = p.N - 1 - n0, limA = p.T - 1 - t0;   // rows past N or T re-read the last row
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = it * 32 + dma_row;
+      offW[it] = static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + dma_chunk;
+      offA[it] = static_cast<uint32_t>(min(r, limA)) * rowA + dma_chunk;
     }
+  };
+  auto issue = [&](uint8_t* buf, int kb) {   // kb < KB
+    int kr = kb + dkb0;
+    kr -= kr >= KB ? KB : 0;
+    const uint8_t* bW = dW + static_cast<uint32_t>(kr) * kBK;
+    const uint8_t* bA = dA + static_cast<uint32_t>(kr) * kBK;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rb = it * 32 + wave * 8;
+      __builtin_amdgcn_global_load_lds(bW + offW[it], (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bA + offA[it], (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
+    }
+  };
+
+  // ---- scales: thread tid owns W row tid and A row tid of a tile; slot s of
+  // a buffer holds stage s (loop stage kb reads slot (kb + kb0) mod KB)
+  constexpr int kScStep = 2 * 2 * 32 * 4;
+  constexpr int kScOp = 2 * 32 * 4;
+  constexpr int kScBuf = kScaleWin * kScStep;
+  uint8_t* const sc_dst = &lds_sc[0][0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
+  uint4 lw0, lw1, la0, la1;
+  auto load_scales = [&](int g, int t0, int n0) {   // into registers; KB bytes per row
+    const uint8_t* sW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, p.N - 1 - n0)) * KB;
+    const uint8_t* sA = p.sa + (static_cast<size_t>(t0 + min(tid, p.T - 1 - t0)) * p.G + g) * KB;
+    lw0 = *reinterpret_cast<const uint4*>(sW);
+    la0 = *reinterpret_cast<const uint4*>(sA);
+    lw1 = make_uint4(0, 0, 0, 0);
+    la1 = lw1;
+    if (KB > 16) {
+      lw1 = *reinterpret_cast<const uint4*>(sW + 16);
+      la1 = *reinterpret_cast<const uint4*>(sA + 16);
+    }
+  };
+  auto store_scales = [&](int sb) {              // registers -> LDS buffer sb
+    uint8_t* dst = sc_dst + sb * kScBuf;
+    const uint32_t ww[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
+    const uint32_t aw[8] = {la0.x, la0.y, la0.z, la0.w, la1.x, la1.y, la1.z, la1.w};
+#pragma unroll
+    for (int s = 0; s < kScaleWin; ++s) {        // slots past the last stage are never read
+      const int bw = static_cast<int>((ww[s >> 2] >> (8 * (s & 3))) & 0xFF);
+      const int ba = static_cast<int>((aw[s >> 2] >> (8 * (s & 3))) & 0xFF);
+      dst[s * kScStep] = static_cast<uint8_t>(bw);
+      dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(ba) : ba);
+    }
+  };
+  auto read_scales = [&](int kb, int kb0, int sb, uint32_t& swv, uint32_t& sav) {
+    int ks = kb + kb0;
+    ks -= ks >= KB ? KB : 0;
+    swv = *reinterpret_cast<const uint32_t*>(&lds_sc[sb][ks][0][wn][(lane & 31)][0]);
+    sav = *reinterpret_cast<const uint32_t*>(&lds_sc[sb][ks][1][wt][(lane & 31)][0]);
+  };
+
+  // ---- fragments and MFMAs (as bmm_large_kernel)
+  const int r32 = lane & 31;
+  const int q2 = lane >> 5;
+  const int rdW = (wn * 128 + r32) * kBK;
+  const int rdA = kOpBytes + (wt * 128 + r32) * kBK;
+  const int sz = swz8(r32);
+  const int ch00 = (q2 ^ sz) << 4, ch01 = ((q2 + 2) ^ sz) << 4;
+  const int ch10 = ((4 + q2) ^ sz) << 4, ch11 = ((6 + q2) ^ sz) << 4;
+  v8i fw[2][4], fa[2][4];
+  auto read_frag = [&](const uint8_t* q, int c0, int c1) {
+    return make_v8i(*reinterpret_cast<const uint4*>(q + c0), *reinterpret_cast<const uint4*>(q + c1));
+  };
+  auto read_half = [&](const uint8_t* buf, int c0, int c1, v8i (&w)[4], v8i (&a)[4]) {
+    const uint8_t* qw = buf + rdW;
+    const uint8_t* qa = buf + rdA;
+    w[0] = read_frag(qw, c0, c1);
+    a[0] = read_frag(qa, c0, c1);
+    a[1] = read_frag(qa + 32 * kBK, c0, c1);
+    w[1] = read_frag(qw + 32 * kBK, c0, c1);
+    a[2] = read_frag(qa + 64 * kBK, c0, c1);
+    w[2] = read_frag(qw + 64 * kBK, c0, c1);
+    a[3] = read_frag(qa + 96 * kBK, c0, c1);
+    w[3] = read_frag(qw + 96 * kBK, c0, c1);
+  };
+  v16f acc[4][4];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav) {
+    mfma_ij<0, 0>(acc, w, a, swv, sav);
+    mfma_ij<0, 1>(acc, w, a, swv, sav);
+    mfma_ij<1, 0>(acc, w, a, swv, sav);
+    mfma_ij<1, 1>(acc, w, a, swv, sav);
+    mfma_ij<0, 2>(acc, w, a, swv, sav);
+    mfma_ij<1, 2>(acc, w, a, swv, sav);
+    mfma_ij<2, 0>(acc, w, a, swv, sav);
+    mfma_ij<2, 1>(acc, w, a, swv, sav);
+    mfma_ij<2, 2>(acc, w, a, swv, sav);
+    mfma_ij<0, 3>(acc, w, a, swv, sav);
+    mfma_ij<1, 3>(acc, w, a, swv, sav);
+    mfma_ij<2, 3>(acc, w, a, swv, sav);
+    mfma_ij<3, 0>(acc, w, a, swv, sav);
+    mfma_ij<3, 1>(acc, w, a, swv, sav);
+    mfma_ij<3, 2>(acc, w, a, swv, sav);
+    mfma_ij<3, 3>(acc, w, a, swv, sav);
+  };
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
+  };
+  constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
+  constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
+  constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
+
+  // front / back: the two halves of a stage, as in bmm_large_kernel.  back()
+  // fetches stage `dma_kb` of the DMA tile into `cur` and reads the scales of
+  // stage rs_kb (rotation rs_kb0, buffer rs_sb) with the first half of the
+  // next stage from `nxt`.
+  uint32_t swv, sav;
+  auto front = [&](const uint8_t* cur) {
+    __builtin_amdgcn_sched_barrier(0);
+    mma_half(fw[0], fa[0], swv, sav);
+    read_half(cur, ch10, ch11, fw[1], fa[1]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    pin_acc();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+  };
+  auto back = [&](uint8_t* cur, const uint8_t* nxt, int dma_kb, int rs_kb, int rs_kb0, int rs_sb) {
+    // the scale reads go before the DMA: with a run-time buffer index the
+    // compiler cannot tell them from the DMA's target and would make them
+    // wait for it
+    uint32_t swv1, sav1;
+    read_scales(rs_kb, rs_kb0, rs_sb, swv1, sav1);
+    issue(cur, dma_kb);
+    mma_half(fw[1], fa[1], swv, sav);
+    read_half(nxt, ch00, ch01, fw[0], fa[0]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the two scale reads
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    pin_acc();
+    __builtin_amdgcn_sched_barrier(0);
+    swv = swv1;
+    sav = sav1;
+  };
+
+  // ---- first tile: prologue
+  int cg, ct0, cn0, ckb0;
+  if (!tile_at(0, cg, ct0, cn0, ckb0)) return;
+  int csb = 0;
+  set_dma_tile(cg, ct0, cn0, ckb0);
+  issue(st0, 0);
+  load_scales(cg, ct0, cn0);
+  issue(st1, 1);
+  store_scales(0);                               // waits for the scale loads (after stage 0's DMA)
+  __builtin_amdgcn_s_waitcnt(kWaitNewest16);
+  __builtin_amdgcn_s_barrier();
+  read_scales(0, ckb0, 0, swv, sav);
+  read_half(st0, ch00, ch01, fw[0], fa[0]);
+  zero_acc();
+
+  for (int r = 0;; ++r) {
+    front(st0);                                  // stage 0 (first half)
+    int kb = 0;
+    for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
+      back(st0, st1, kb + 2, kb + 1, ckb0, csb);
+      front(st1);
+      back(st1, st0, kb + 3, kb + 2, ckb0, csb);
+      front(st0);
+    }
+    // stages KB-2 (begun) and KB-1 remain; fetch the next tile meanwhile
+    int ng, nt0, nn0, nkb0;
+    const bool more = tile_at(r + 1, ng, nt0, nn0, nkb0);
+    if (!more) {                                 // refetch this tile: harmless, never read
+      ng = cg;
+      nt0 = ct0;
+      nn0 = cn0;
+      nkb0 = ckb0;
+    }
+    set_dma_tile(ng, nt0, nn0, nkb0);
+    load_scales(ng, nt0, nn0);
+    back(st0, st1, 0, KB - 1, ckb0, csb);        // next tile's stage 0 -> st0
+    front(st1);                                  // waits for it and for the scale loads
+    store_scales(csb ^ 1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    __builtin_amdgcn_s_barrier();
+    back(st1, st0, 1, 0, nkb0, csb ^ 1);         // next tile's stage 1 -> st1; its stage 0 half 0
+
+    // epilogue of this tile, straight from the accumulators (see bmm_large_kernel)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = ct0 + wt * 128 + j * 32 + r32;
+      uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + cg) * p.N;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v16f& v = acc[i][j];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+          const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          const int n = cn0 + wn * 128 + i * 32 + pp * 16 + q2 * 8;
+          if (t < p.T && n < p.N)
+            *reinterpret_cast<uint4*>(orow + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+        }
+      }
+    }
+    if (!more) break;
+    zero_acc();
+    cg = ng;
+    ct0 = nt0;
+    cn0 = nn0;
+    ckb0 = nkb0;
+    csb ^= 1;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);          // no DMA outlives the workgroup
 }
 
 // ----------------------------------------------------------- small T (<= 64)
@@ -502,11 +836,25 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
   p.tiles_n = (N + kLN - 1) / kLN;
   p.total_tiles = p.tiles_t * p.tiles_n * G;
   p.per_xcd = (p.total_tiles + 7) / 8;
-  const int grid = p.per_xcd * 8;
-  if (fnuz)
-    bmm_large_kernel<true><<<grid, 256, 0, stream>>>(p);
-  else
-    bmm_large_kernel<false><<<grid, 256, 0, stream>>>(p);
+  const int KB = K / kBK;
+  const int cus = device_cu_count();
+  const bool persistent = (KB == 16 || KB == 32) && cus >= 8 && aligned(sa, 16) && aligned(sw, 16);
+  if (persistent) {
+    // one resident workgroup per compute unit, XCD-major (workgroup i runs on XCD i % 8)
+    p.wg_per_xcd = std::min(p.per_xcd, cus / 8);
+    const int grid = p.wg_per_xcd * 8;
+    if (fnuz)
+      bmm_persistent_kernel<true><<<grid, 256, 0, stream>>>(p);
+    else
+      bmm_persistent_kernel<false><<<grid, 256, 0, stream>>>(p);
+  } else {
+    p.wg_per_xcd = 0;
+    const int grid = p.per_xcd * 8;
+    if (fnuz)
+      bmm_large_kernel<true><<<grid, 256, 0, stream>>>(p);
+    else
+      bmm_large_kernel<false><<<grid, 256, 0, stream>>>(p);
+  }
   count(C_BMM_LARGE);
   return launch_status("mx_bmm_a8w8_mxscale");
 }

@@ -19,6 +19,8 @@ void clear_error();
 bool dry_run();
 // Checks that the current HIP device is a gfx950 (cached per device).
 mx_status require_gfx950();
+// Compute units of the current device (known once require_gfx950() passed; 0 if not).
+int device_cu_count();
 // Maps a launch error to MX_ERR_HIP with a message naming `what`.
 mx_status launch_status(const char* what);
 

@@ -58,6 +58,41 @@ def test_random_operands(T, Gn, N, K):
     assert_gemm_close(out, ref, f"T={T} G={Gn} N={N} K={K}")
 
 
+# K = 2048 and 4096 (16 or 32 K-stages) take the persistent kernel: tile counts
+# below one per XCD, one per workgroup, and several per workgroup (T = 4200:
+# 340 tiles on 256 workgroups), with ragged T and N tiles.  Large cases are
+# checked on sampled rows (first, last, tile edges and random ones).
+PERSIST_SHAPES = [(300, 1, 272, 2048), (1000, 3, 512, 4096), (4200, 5, 1024, 2048), (2600, 2, 784, 4096)]
+
+
+def _sample_rows(T, rng, n=48):
+    edges = [0, T - 1] + [t for t in range(255, T, 256)] + [t for t in range(256, T, 256)]
+    return np.unique(np.concatenate([np.array(edges), rng.integers(0, T, n)]))
+
+
+@pytest.mark.parametrize("T,Gn,N,K", PERSIST_SHAPES)
+def test_persistent_tiles(T, Gn, N, K):
+    a, sa, w, sw = workloads.gemm_operands(2000 + T + K, T, Gn, N, K)
+    say("bmm persistent", T, Gn, N, K)
+    out = _gpu_bmm(a, sa, w, sw)
+    rows = _sample_rows(T, np.random.default_rng(T)) if T * Gn * N * K > 2 ** 31 else np.arange(T)
+    ref = G.bmm_a8w8_mxscale(a[rows], sa[rows], w, sw)
+    assert_gemm_close(out[rows], ref, f"T={T} G={Gn} N={N} K={K}")
+
+
+def test_persistent_fnuz_bit_identical():
+    T, Gn, N, K = 600, 2, 512, 4096
+    a, sa, w, sw = workloads.gemm_operands(31, T, Gn, N, K, a_exp=(-12, -2))
+    a_fnuz = np.where(a == 0x80, 0, a).astype(np.uint8)
+    sa_fnuz = (sa.astype(int) + 1).astype(np.uint8)
+    say("bmm persistent fnuz")
+    o_ocp = _gpu_bmm(a, sa, w, sw)
+    o_fnuz = _gpu_bmm(a_fnuz, sa_fnuz, w, sw, mx.MX_FP8_E4M3_FNUZ)
+    assert np.array_equal(o_ocp, o_fnuz)
+    rows = _sample_rows(T, np.random.default_rng(1))
+    assert_gemm_close(o_fnuz[rows], G.bmm_a8w8_mxscale(a_fnuz[rows], sa_fnuz[rows], w, sw, a_fmt=F.FNUZ), "fnuz")
+
+
 @pytest.mark.parametrize("T", [40, 300])
 def test_fnuz_activations(T):
     Gn, N, K = 2, 256, 512
