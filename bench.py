@@ -50,6 +50,22 @@ def bmm_bytes(T, G, N, K):
     return T * G * K + T * G * K // 128 + G * N * K + G * N * K // 128 + T * G * N * 2
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or None
+    when the summary is missing or the kernel's source changed since."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "wo_a_T8192_hbm_bytes.md")
+    try:
+        text = open(path).read()
+        rec = json.loads(re.search(r"^traffic-json: (.*)$", text, re.M).group(1))[kernel]
+        src = open(os.path.join(ROOT, rec["src"]), "rb").read()
+    except (OSError, AttributeError, KeyError, ValueError):
+        return None
+    return rec["bytes"] if hashlib.sha256(src).hexdigest() == rec["src_sha256"] else None
+
+
 class Timer:
     """HIP events recorded on the given torch stream (the stream the library launches on)."""
 
@@ -256,7 +272,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--extra", action="store_true", help="also time decode, MXFP8 linear, dequant")
     ap.add_argument("--long", action="store_true", help="also time the 100,000-token chunked prefill")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -292,6 +308,9 @@ def main():
     qq = np.percentile(r["q_ms"] * 1e3, [0, 50, 100])
     log(f"[bench] per-launch min/median/max: bmm {bq[0]:.1f}/{bq[1]:.1f}/{bq[2]:.1f} us, "
         f"quant {qq[0]:.1f}/{qq[1]:.1f}/{qq[2]:.1f} us")
+    # the library runs the persistent large-tile kernel for K = 2048 and 4096
+    # (16-byte aligned scales, as here), the one-tile-per-workgroup kernel otherwise
+    bmm_kernel = "bmm_persistent_kernel" if p.K in (2048, 4096) else "bmm_large_kernel"
     rec = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -310,11 +329,12 @@ def main():
         "pct_fp8_peak": round(100 * tflops / PEAK_FP8_TFLOPS, 2),
         "quant_hbm_GBps": round(q_gbs, 1),
         "quant": {"us": round(q_avg_ms * 1e3, 2), "GBps": round(q_gbs, 1), "frac": round(q_gbs / PEAK_HBM_GBS, 4),
-                  "algorithmic_bytes": qb},
-        "roofline": {"bound": "mfma", "kernel": "bmm_large_kernel", "achieved": round(b_ach, 1),
+                  "algorithmic_bytes": qb, "traffic": measured_traffic("quant_kernel")},
+        "roofline": {"bound": "mfma", "kernel": bmm_kernel, "achieved": round(b_ach, 1),
                      "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": round(b_ach / PEAK_FP8_TFLOPS, 4),
+                     "traffic": measured_traffic(bmm_kernel),
                      "launch_us": round(b_avg_ms * 1e3, 2), "algorithmic_flops": p.flops,
-                     "algorithmic_bytes": bmm_bytes(p.T, p.G, p.N, p.K), "traffic": None},
+                     "algorithmic_bytes": bmm_bytes(p.T, p.G, p.N, p.K)},
         "wall_s_timed_region": round(r["wall_s"], 4),
     }
     if not args.no_cpu_baseline:
