@@ -726,35 +726,84 @@ struct SmallArgs {
   int n_groups;          // ceil(N / (16*NT))
 };
 
-// One workgroup: all T (<= 64) rows x 16*NT columns n of one group g.  Wave w
-// takes K-steps w, w+4, ...; partial sums meet in LDS.
+constexpr int kSmallWaves = 4;
+constexpr int kSmallThreads = 64 * kSmallWaves;
+
+// One workgroup: all T (<= 64) rows x 16*NT columns n of one group g, kSmallWaves
+// waves (two per SIMD).  Wave w takes K-steps w, w+kSmallWaves, ...; partial
+// sums meet in LDS.  The workgroup's scale
+// rows are staged in LDS once (W rows n0.. are one contiguous block; A rows
+// one per token), so the loop reads only operand bytes from memory; the
+// operands of a wave's next K-step are loaded while the current one's MFMAs run.
 template <int NT, int SB, bool A_FNUZ>
-__global__ __launch_bounds__(256) void bmm_small_kernel(SmallArgs p) {
-  __shared__ float red[4][NT * 4][4][64];   // [wave][tile][reg][lane]
+__global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
+  __shared__ float red[4][NT * 4][4][64];   // [wave % 4][tile][reg][lane]
+  extern __shared__ uint8_t scl[];          // [16*NT W rows | 64 A rows][SPK]
   const int g = blockIdx.x / p.n_groups;
   const int n0 = (blockIdx.x % p.n_groups) * (16 * NT);
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave-uniform (a scalar): the K loop below is then a uniform loop
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = p.K / kBK;
   const int SPK = p.K / SB;                   // scale bytes per row
   const int kq = lane >> 4;                   // lane group: K bytes 16kq.. and 64+16kq.., scale block kq
   const size_t rowA = static_cast<size_t>(p.G) * p.K;
+  constexpr int kRowsW = 16 * NT;
+
+  // ---- stage the scales: rows past N or T repeat the last valid row
+  {
+    const int nW = min(kRowsW, p.N - n0);
+    const uint8_t* srcW = p.sw + (static_cast<size_t>(g) * p.N + n0) * SPK;
+    if ((SPK & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.sw) | reinterpret_cast<uintptr_t>(p.sa)) & 3) == 0) {
+      const int dw = SPK >> 2;                // dwords per row
+      for (int e = tid; e < kRowsW * dw; e += kSmallThreads) {
+        const int r = e / dw, c = e - r * dw;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(srcW + static_cast<size_t>(min(r, nW - 1)) * SPK + 4 * c);
+        *reinterpret_cast<uint32_t*>(scl + r * SPK + 4 * c) = v;
+      }
+      for (int e = tid; e < 64 * dw; e += kSmallThreads) {
+        const int r = e / dw, c = e - r * dw;
+        const int t = min(r, p.T - 1);
+        uint32_t v = *reinterpret_cast<const uint32_t*>(p.sa + (static_cast<size_t>(t) * p.G + g) * SPK + 4 * c);
+        if (A_FNUZ) {
+          uint32_t o = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) o |= static_cast<uint32_t>(fnuz_scale_to_ocp((v >> (8 * b)) & 0xFF)) << (8 * b);
+          v = o;
+        }
+        *reinterpret_cast<uint32_t*>(scl + (kRowsW + r) * SPK + 4 * c) = v;
+      }
+    } else {
+      for (int e = tid; e < kRowsW * SPK; e += kSmallThreads) {
+        const int r = e / SPK, c = e - r * SPK;
+        scl[r * SPK + c] = srcW[static_cast<size_t>(min(r, nW - 1)) * SPK + c];
+      }
+      for (int e = tid; e < 64 * SPK; e += kSmallThreads) {
+        const int r = e / SPK, c = e - r * SPK;
+        const int t = min(r, p.T - 1);
+        const int v = p.sa[(static_cast<size_t>(t) * p.G + g) * SPK + c];
+        scl[(kRowsW + r) * SPK + c] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(v) : v);
+      }
+    }
+  }
+  __syncthreads();
 
   const uint8_t* pw[NT];
-  const uint8_t* psw[NT];
+  const uint8_t* lsw[NT];
 #pragma unroll
   for (int i = 0; i < NT; ++i) {
     const int n = min(n0 + i * 16 + (lane & 15), p.N - 1);
     pw[i] = p.w + (static_cast<size_t>(g) * p.N + n) * p.K + kq * 16;
-    psw[i] = p.sw + (static_cast<size_t>(g) * p.N + n) * SPK + (SB == 32 ? kq : 0);
+    lsw[i] = scl + (i * 16 + (lane & 15)) * SPK + (SB == 32 ? kq : 0);
   }
   const uint8_t* pa[4];
-  const uint8_t* psa[4];
+  const uint8_t* lsa[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int t = min(j * 16 + (lane & 15), p.T - 1);
     pa[j] = p.a + static_cast<size_t>(t) * rowA + static_cast<size_t>(g) * p.K + kq * 16;
-    psa[j] = p.sa + (static_cast<size_t>(t) * p.G + g) * SPK + (SB == 32 ? kq : 0);
+    lsa[j] = scl + (kRowsW + j * 16 + (lane & 15)) * SPK + (SB == 32 ? kq : 0);
   }
   constexpr int kScalesPerStep = kBK / SB;
 
@@ -764,36 +813,78 @@ __global__ __launch_bounds__(256) void bmm_small_kernel(SmallArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int kt = wave; kt < KB; kt += 4) {
+  // Two K-steps of operands in registers: the loads of this wave's next step
+  // are in flight while the MFMAs of the current one run.  Steps past the end
+  // load a clamped, valid step whose data is never used.
+  v8i fw[2][NT], fa[2][4];
+  auto load = [&](int kt, int b) {
+    kt = min(kt, KB - 1);
     const size_t ko = static_cast<size_t>(kt) * kBK;
-    v8i fw[NT], fa[4];
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+      fw[b][i] = make_v8i(*reinterpret_cast<const uint4*>(pw[i] + ko), *reinterpret_cast<const uint4*>(pw[i] + ko + 64));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      fa[b][j] = make_v8i(*reinterpret_cast<const uint4*>(pa[j] + ko), *reinterpret_cast<const uint4*>(pa[j] + ko + 64));
+  };
+  auto compute = [&](int kt, int b) {
     int s_w[NT], s_a[4];
 #pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      fw[i] = make_v8i(*reinterpret_cast<const uint4*>(pw[i] + ko), *reinterpret_cast<const uint4*>(pw[i] + ko + 64));
-      s_w[i] = psw[i][kt * kScalesPerStep];
-    }
+    for (int i = 0; i < NT; ++i) s_w[i] = lsw[i][kt * kScalesPerStep];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      fa[j] = make_v8i(*reinterpret_cast<const uint4*>(pa[j] + ko), *reinterpret_cast<const uint4*>(pa[j] + ko + 64));
-      const int s = psa[j][kt * kScalesPerStep];
-      s_a[j] = A_FNUZ ? fnuz_scale_to_ocp(s) : s;
-    }
+    for (int j = 0; j < 4; ++j) s_a[j] = lsa[j][kt * kScalesPerStep];
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_scaled(fw[i], fa[j], acc[i][j], s_w[i], s_a[j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_scaled(fw[b][i], fa[b][j], acc[i][j], s_w[i], s_a[j]);
+  };
+  constexpr int W = kSmallWaves;
+  load(wave, 0);
+  load(wave + W, 1);
+  int kt = wave;
+  for (; kt + W < KB; kt += 2 * W) {          // branch-free body: both steps exist
+    compute(kt, 0);
+    load(kt + 2 * W, 0);
+    compute(kt + W, 1);
+    load(kt + 3 * W, 1);
   }
+  if (kt < KB) compute(kt, 0);                // a last single step (buffer 0 holds it)
+  __builtin_amdgcn_s_waitcnt(0x0070);         // the clamped prefetches end here too
 
+  // reduce over the waves in two rounds through 4 slots: waves 4..7 hand
+  // their sums to waves 0..3, which then meet in the slots
+  static_assert(kSmallWaves == 4 || kSmallWaves == 8, "one or two reduction rounds of four");
+  if (kSmallWaves == 8 && wave >= 4) {
 #pragma unroll
-  for (int i = 0; i < NT; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][i * 4 + j][r][lane] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) red[wave - 4][i * 4 + j][r][lane] = acc[i][j][r];
+  }
+  if (kSmallWaves == 8) {
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += red[wave][i * 4 + j][r][lane];
+    }
+    __syncthreads();
+  }
+  if (wave < 4) {
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][i * 4 + j][r][lane] = acc[i][j][r];
+  }
   __syncthreads();
-  // wave w finalises tiles w, w+4, ...
-  for (int tile = wave; tile < NT * 4; tile += 4) {
+  // wave w < 4 finalises tiles w, w+4, ...
+  for (int tile = wave; tile < NT * 4 && wave < 4; tile += 4) {
     const int i = tile / 4, j = tile % 4;
     v4f s;
 #pragma unroll
@@ -806,13 +897,19 @@ __global__ __launch_bounds__(256) void bmm_small_kernel(SmallArgs p) {
   }
 }
 
+// LDS the small-T kernel stages its scale rows in (dynamic shared memory).
+constexpr size_t kSmallScaleLdsMax = 48 * 1024;
+template <int NT, int SB>
+constexpr size_t small_scale_lds(int K) { return static_cast<size_t>(16 * NT + 64) * (K / SB); }
+
 template <int NT, int SB>
 void launch_small(const SmallArgs& a, bool fnuz, hipStream_t s) {
   const int grid = a.G * a.n_groups;
+  const size_t lds = small_scale_lds<NT, SB>(a.K);   // staged scale rows
   if (fnuz)
-    bmm_small_kernel<NT, SB, true><<<grid, 256, 0, s>>>(a);
+    bmm_small_kernel<NT, SB, true><<<grid, kSmallThreads, lds, s>>>(a);
   else
-    bmm_small_kernel<NT, SB, false><<<grid, 256, 0, s>>>(a);
+    bmm_small_kernel<NT, SB, false><<<grid, kSmallThreads, lds, s>>>(a);
 }
 
 }  // namespace
@@ -822,7 +919,7 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
                      void* out, int64_t T, int32_t G, int32_t N, int32_t K, hipStream_t stream) {
   if (T == 0) return MX_OK;
   const bool fnuz = a_fmt == MX_FP8_E4M3_FNUZ;
-  if (T <= 64) {
+  if (T <= 64 && small_scale_lds<4, 128>(K) <= kSmallScaleLdsMax) {   // (else the tiled kernels)
     SmallArgs s{a, sa, w, sw, static_cast<uint16_t*>(out), static_cast<int>(T), G, N, K, (N + 63) / 64};
     launch_small<4, 128>(s, fnuz, stream);
     count(C_BMM_SMALL);
@@ -864,6 +961,9 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
+  if (small_scale_lds<1, 32>(static_cast<int>(K)) > kSmallScaleLdsMax)
+    return fail(MX_ERR_UNSUPPORTED, "mx_linear: K = %lld is too large for the block-scaled FP8 path (at most %zu)",
+                static_cast<long long>(K), kSmallScaleLdsMax / 80 * 32);
   SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
               static_cast<int>(K), static_cast<int>((N + 15) / 16)};
   launch_small<1, 32>(s, false, stream);
