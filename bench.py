@@ -225,7 +225,96 @@ def bench_extra(mx, torch, workloads, reps=50):
     us_dq, _ = timeit(lambda i: mx.mx_dequant_mxfp8_to_bf16(wd, wsd))
     res["dequant_5120x576"] = {"us": us_dq, "GBps": (5120 * 576 * 3 + 5120 * 18) / us_dq / 1e3,
                                "algorithmic_bytes": 5120 * 576 * 3 + 5120 * 18}
+    res["graph_40_calls"] = bench_graphs(mx, torch, workloads)
     return res
+
+
+def bench_graphs(mx, torch, workloads, calls=40, replays=20):
+    """Device-side cost per call of the latency-bound workloads: a sequence of
+    `calls` calls on `calls` distinct weight copies (a 40-layer stack) captured
+    in one HIP graph and replayed; time per call = replay time / calls."""
+    dev = torch.device("cuda:0")
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    out = {}
+
+    def time_graph(record):
+        s = torch.cuda.Stream(device=dev)
+        s.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(s):             # warm-up outside the graph
+            record()
+        torch.cuda.current_stream(dev).wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            record()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(replays):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / replays / calls
+
+    # decode batch: one weight copy per call (40 x 64.5 MiB)
+    p = workloads.decode_batch()
+    cos, sin = workloads.rope_tables(rows=32768)
+    x, cosd, sind = u16(p.x), u16(cos), u16(sin)
+    pos = torch.from_numpy(p.positions).to(dev)
+    w0, ws0 = torch.from_numpy(p.w).to(dev), torch.from_numpy(p.w_scale).to(dev)
+    ws = [(w0.clone(), ws0.clone()) for _ in range(calls)]
+    L = p.H * p.D
+    q = torch.empty((p.T, L), dtype=torch.uint8, device=dev)
+    s = torch.empty((p.T, L // 128), dtype=torch.uint8, device=dev)
+    o = torch.empty((p.T, p.G, p.N), dtype=torch.bfloat16, device=dev)
+
+    def rec_decode():
+        for w, sw in ws:
+            mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, q=q, scale=s)
+            mx.mx_bmm_a8w8_mxscale(q.view(p.T, p.G, p.K), s.view(p.T, p.G, -1), w, sw, out=o)
+    us = time_graph(rec_decode)
+    bb = bmm_bytes(p.T, p.G, p.N, p.K) + quant_bytes(p.T, L)
+    out["decode_T64_quant_plus_bmm"] = {"us_per_call": us, "GBps": bb / us / 1e3, "hbm_frac": bb / us / 1e3 / PEAK_HBM_GBS}
+    del ws, x, q, s, o
+
+    # MXFP8 linear, M = 64, N = 4096, each K
+    data = workloads.mxfp8_linear()
+    lin = {}
+    for K, (xh, wh, wsh, _) in data.items():
+        xd, wd, wsd = u16(xh), torch.from_numpy(wh).to(dev), torch.from_numpy(wsh).to(dev)
+        M, N = xh.shape[0], wh.shape[0]
+        wprep = mx.mx_dequant_mxfp8_to_bf16(wd, wsd) if K % 128 else wd
+        copies = [(wprep.clone(), wsd.clone()) for _ in range(calls)]
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(max(1, mx.mx_linear_workspace_bytes(M, N, K, wprep.element_size())), dtype=torch.uint8,
+                          device=dev)
+
+        def rec_linear():
+            for w, sw in copies:
+                mx.mx_linear(xd, w, sw, out=o, workspace=wsp)
+        us = time_graph(rec_linear)
+        wbytes = N * K * 2 if K % 128 else N * K + N * K // 32
+        lb = wbytes + M * K * 2 + M * N * 2
+        lin[f"K{K}"] = {"us_per_call": us, "GBps": lb / us / 1e3, "hbm_frac": lb / us / 1e3 / PEAK_HBM_GBS}
+        del copies, wprep
+    out["mxfp8_linear_M64_N4096"] = lin
+
+    # load-time dequantisation, the pages' 5120 x 576 weight, 40 layers
+    rng = np.random.default_rng(21)
+    wd = torch.from_numpy(workloads.weight_codes(rng, (5120, 576))).to(dev)
+    wsd = torch.from_numpy(workloads.scale_bytes(rng, (5120, 18), -10, -4)).to(dev)
+    copies = [(wd.clone(), wsd.clone(), torch.empty((5120, 576), dtype=torch.bfloat16, device=dev))
+              for _ in range(calls)]
+
+    def rec_dq():
+        for w, sw, ob in copies:
+            mx.mx_dequant_mxfp8_to_bf16(w, sw, out=ob)
+    us = time_graph(rec_dq)
+    db = 5120 * 576 * 3 + 5120 * 18
+    out["dequant_5120x576"] = {"us_per_call": us, "GBps": db / us / 1e3, "hbm_frac": db / us / 1e3 / PEAK_HBM_GBS}
+    return out
 
 
 def bench_long(mx, torch, workloads):
