@@ -751,43 +751,6 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
   const size_t rowA = static_cast<size_t>(p.G) * p.K;
   constexpr int kRowsW = 16 * NT;
 
-  // ---- stage the scales: rows past N or T repeat the last valid row
-  {
-    const int nW = min(kRowsW, p.N - n0);
-    const uint8_t* srcW = p.sw + (static_cast<size_t>(g) * p.N + n0) * SPK;
-    if ((SPK & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.sw) | reinterpret_cast<uintptr_t>(p.sa)) & 3) == 0) {
-      const int dw = SPK >> 2;                // dwords per row
-      for (int e = tid; e < kRowsW * dw; e += kSmallThreads) {
-        const int r = e / dw, c = e - r * dw;
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(srcW + static_cast<size_t>(min(r, nW - 1)) * SPK + 4 * c);
-        *reinterpret_cast<uint32_t*>(scl + r * SPK + 4 * c) = v;
-      }
-      for (int e = tid; e < 64 * dw; e += kSmallThreads) {
-        const int r = e / dw, c = e - r * dw;
-        const int t = min(r, p.T - 1);
-        uint32_t v = *reinterpret_cast<const uint32_t*>(p.sa + (static_cast<size_t>(t) * p.G + g) * SPK + 4 * c);
-        if (A_FNUZ) {
-          uint32_t o = 0;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) o |= static_cast<uint32_t>(fnuz_scale_to_ocp((v >> (8 * b)) & 0xFF)) << (8 * b);
-          v = o;
-        }
-        *reinterpret_cast<uint32_t*>(scl + (kRowsW + r) * SPK + 4 * c) = v;
-      }
-    } else {
-      for (int e = tid; e < kRowsW * SPK; e += kSmallThreads) {
-        const int r = e / SPK, c = e - r * SPK;
-        scl[r * SPK + c] = srcW[static_cast<size_t>(min(r, nW - 1)) * SPK + c];
-      }
-      for (int e = tid; e < 64 * SPK; e += kSmallThreads) {
-        const int r = e / SPK, c = e - r * SPK;
-        const int t = min(r, p.T - 1);
-        const int v = p.sa[(static_cast<size_t>(t) * p.G + g) * SPK + c];
-        scl[(kRowsW + r) * SPK + c] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(v) : v);
-      }
-    }
-  }
-  __syncthreads();
 
   const uint8_t* pw[NT];
   const uint8_t* lsw[NT];
@@ -839,8 +802,81 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
       for (int j = 0; j < 4; ++j) acc[i][j] = mfma_scaled(fw[b][i], fa[b][j], acc[i][j], s_w[i], s_a[j]);
   };
   constexpr int W = kSmallWaves;
-  load(wave, 0);
+  load(wave, 0);                              // the first operands fly while the scales are staged
   load(wave + W, 1);
+
+  // ---- stage the scales: rows past N or T repeat the last valid row
+  {
+    const int nW = min(kRowsW, p.N - n0);
+    const uint8_t* srcW = p.sw + (static_cast<size_t>(g) * p.N + n0) * SPK;
+    if ((SPK & 3) == 0 && ((reinterpret_cast<uintptr_t>(p.sw) | reinterpret_cast<uintptr_t>(p.sa)) & 3) == 0) {
+      const int dw = SPK >> 2;                // dwords per row
+      const int nw = kRowsW * dw, na = 64 * dw;
+      // all loads first (one round trip), then the LDS writes; up to kPer
+      // dwords per thread per operand that way, a loop for anything beyond
+      constexpr int kPer = 8;
+      uint32_t vw[kPer], va[kPer];
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kSmallThreads;
+        if (e < nw) {
+          const int r = e / dw, c = e - r * dw;
+          vw[u] = *reinterpret_cast<const uint32_t*>(srcW + static_cast<size_t>(min(r, nW - 1)) * SPK + 4 * c);
+        }
+        if (e < na) {
+          const int r = e / dw, c = e - r * dw;
+          va[u] = *reinterpret_cast<const uint32_t*>(p.sa + (static_cast<size_t>(min(r, p.T - 1)) * p.G + g) * SPK + 4 * c);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int e = tid + u * kSmallThreads;
+        if (e < nw) {
+          const int r = e / dw, c = e - r * dw;
+          *reinterpret_cast<uint32_t*>(scl + r * SPK + 4 * c) = vw[u];
+        }
+        if (e < na) {
+          const int r = e / dw, c = e - r * dw;
+          uint32_t v = va[u];
+          if (A_FNUZ) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) o |= static_cast<uint32_t>(fnuz_scale_to_ocp((v >> (8 * b)) & 0xFF)) << (8 * b);
+            v = o;
+          }
+          *reinterpret_cast<uint32_t*>(scl + (kRowsW + r) * SPK + 4 * c) = v;
+        }
+      }
+      for (int e = tid + kPer * kSmallThreads; e < nw; e += kSmallThreads) {
+        const int r = e / dw, c = e - r * dw;
+        *reinterpret_cast<uint32_t*>(scl + r * SPK + 4 * c) =
+            *reinterpret_cast<const uint32_t*>(srcW + static_cast<size_t>(min(r, nW - 1)) * SPK + 4 * c);
+      }
+      for (int e = tid + kPer * kSmallThreads; e < na; e += kSmallThreads) {
+        const int r = e / dw, c = e - r * dw;
+        uint32_t v = *reinterpret_cast<const uint32_t*>(p.sa + (static_cast<size_t>(min(r, p.T - 1)) * p.G + g) * SPK + 4 * c);
+        if (A_FNUZ) {
+          uint32_t o = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) o |= static_cast<uint32_t>(fnuz_scale_to_ocp((v >> (8 * b)) & 0xFF)) << (8 * b);
+          v = o;
+        }
+        *reinterpret_cast<uint32_t*>(scl + (kRowsW + r) * SPK + 4 * c) = v;
+      }
+    } else {
+      for (int e = tid; e < kRowsW * SPK; e += kSmallThreads) {
+        const int r = e / SPK, c = e - r * SPK;
+        scl[r * SPK + c] = srcW[static_cast<size_t>(min(r, nW - 1)) * SPK + c];
+      }
+      for (int e = tid; e < 64 * SPK; e += kSmallThreads) {
+        const int r = e / SPK, c = e - r * SPK;
+        const int t = min(r, p.T - 1);
+        const int v = p.sa[(static_cast<size_t>(t) * p.G + g) * SPK + c];
+        scl[(kRowsW + r) * SPK + c] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(v) : v);
+      }
+    }
+  }
+  __syncthreads();
   int kt = wave;
   for (; kt + W < KB; kt += 2 * W) {          // branch-free body: both steps exist
     compute(kt, 0);
