@@ -80,6 +80,35 @@ def test_persistent_tiles(T, Gn, N, K):
     assert_gemm_close(out[rows], ref, f"T={T} G={Gn} N={N} K={K}")
 
 
+# the one-tile-per-workgroup kernel: K beyond one 32-stage scale window
+# (restaged in the loop), an odd number of stages, and K = 4096 with scale
+# tensors that are not 16-byte aligned (which keeps the persistent kernel off)
+@pytest.mark.parametrize("T,Gn,N,K", [(300, 1, 272, 8192), (280, 2, 256, 4224), (260, 1, 512, 6272)])
+def test_large_kernel_scale_windows(T, Gn, N, K):
+    a, sa, w, sw = workloads.gemm_operands(3000 + K, T, Gn, N, K)
+    say("bmm large windows", T, Gn, N, K)
+    out = _gpu_bmm(a, sa, w, sw)
+    rows = _sample_rows(T, np.random.default_rng(K))
+    assert_gemm_close(out[rows], G.bmm_a8w8_mxscale(a[rows], sa[rows], w, sw), f"T={T} K={K}")
+
+
+def test_large_kernel_misaligned_scales():
+    T, Gn, N, K = 300, 2, 256, 4096
+    a, sa, w, sw = workloads.gemm_operands(41, T, Gn, N, K)
+    dev = torch.device("cuda:0")
+    say("bmm misaligned scales")
+    # the scale tensors start 1 byte into a larger buffer
+    sab = torch.zeros(sa.size + 16, dtype=torch.uint8, device=dev)
+    swb = torch.zeros(sw.size + 16, dtype=torch.uint8, device=dev)
+    sab[1:1 + sa.size] = torch.from_numpy(sa.reshape(-1)).to(dev)
+    swb[1:1 + sw.size] = torch.from_numpy(sw.reshape(-1)).to(dev)
+    sad = sab[1:1 + sa.size].view(sa.shape)
+    swd = swb[1:1 + sw.size].view(sw.shape)
+    out = mx.mx_bmm_a8w8_mxscale(dev_u8(a), sad, dev_u8(w), swd)
+    torch.cuda.synchronize()
+    assert_gemm_close(host_u16(out), G.bmm_a8w8_mxscale(a, sa, w, sw), "misaligned scales")
+
+
 def test_persistent_fnuz_bit_identical():
     T, Gn, N, K = 600, 2, 512, 4096
     a, sa, w, sw = workloads.gemm_operands(31, T, Gn, N, K, a_exp=(-12, -2))
