@@ -107,11 +107,15 @@ struct LargeArgs {
 // One 32x32x64 block-scaled MFMA of the large kernel: W tile I times A tile
 // J.  The scale operands are 4-byte words holding the scales of tiles 0..3;
 // the byte-select operands pick byte I of the W word and byte J of the A word.
-template <int I, int J>
+// With FIRST the accumulator input is zero: the first MFMA of a tile starts
+// its sum, so the accumulators need no clearing between tiles.
+template <int I, int J, bool FIRST = false>
 __device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
                                         uint32_t sav) {
-  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[I], a[J], acc[I][J], kFmtFp8, kFmtFp8, I,
-                                                             static_cast<int>(swv), J, static_cast<int>(sav));
+  const v16f zero = {};
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[I], a[J], FIRST ? zero : acc[I][J], kFmtFp8,
+                                                             kFmtFp8, I, static_cast<int>(swv), J,
+                                                             static_cast<int>(sav));
 }
 
 template <bool A_FNUZ>
@@ -558,31 +562,24 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     w[3] = read_frag(qw + 96 * kBK, c0, c1);
   };
   v16f acc[4][4];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  };
-  auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav) {
-    mfma_ij<0, 0>(acc, w, a, swv, sav);
-    mfma_ij<0, 1>(acc, w, a, swv, sav);
-    mfma_ij<1, 0>(acc, w, a, swv, sav);
-    mfma_ij<1, 1>(acc, w, a, swv, sav);
-    mfma_ij<0, 2>(acc, w, a, swv, sav);
-    mfma_ij<1, 2>(acc, w, a, swv, sav);
-    mfma_ij<2, 0>(acc, w, a, swv, sav);
-    mfma_ij<2, 1>(acc, w, a, swv, sav);
-    mfma_ij<2, 2>(acc, w, a, swv, sav);
-    mfma_ij<0, 3>(acc, w, a, swv, sav);
-    mfma_ij<1, 3>(acc, w, a, swv, sav);
-    mfma_ij<2, 3>(acc, w, a, swv, sav);
-    mfma_ij<3, 0>(acc, w, a, swv, sav);
-    mfma_ij<3, 1>(acc, w, a, swv, sav);
-    mfma_ij<3, 2>(acc, w, a, swv, sav);
-    mfma_ij<3, 3>(acc, w, a, swv, sav);
+  auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav, auto first) {
+    constexpr bool F = decltype(first)::value;
+    mfma_ij<0, 0, F>(acc, w, a, swv, sav);
+    mfma_ij<0, 1, F>(acc, w, a, swv, sav);
+    mfma_ij<1, 0, F>(acc, w, a, swv, sav);
+    mfma_ij<1, 1, F>(acc, w, a, swv, sav);
+    mfma_ij<0, 2, F>(acc, w, a, swv, sav);
+    mfma_ij<1, 2, F>(acc, w, a, swv, sav);
+    mfma_ij<2, 0, F>(acc, w, a, swv, sav);
+    mfma_ij<2, 1, F>(acc, w, a, swv, sav);
+    mfma_ij<2, 2, F>(acc, w, a, swv, sav);
+    mfma_ij<0, 3, F>(acc, w, a, swv, sav);
+    mfma_ij<1, 3, F>(acc, w, a, swv, sav);
+    mfma_ij<2, 3, F>(acc, w, a, swv, sav);
+    mfma_ij<3, 0, F>(acc, w, a, swv, sav);
+    mfma_ij<3, 1, F>(acc, w, a, swv, sav);
+    mfma_ij<3, 2, F>(acc, w, a, swv, sav);
+    mfma_ij<3, 3, F>(acc, w, a, swv, sav);
   };
   auto pin_acc = [&]() {
 #pragma unroll
@@ -599,9 +596,12 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // stage rs_kb (rotation rs_kb0, buffer rs_sb) with the first half of the
   // next stage from `nxt`.
   uint32_t swv, sav;
-  auto front = [&](const uint8_t* cur) {
+  // front(cur, first, with_scales): `first` starts the tile's sums;
+  // `with_scales` also writes the next tile's staged scales (load_scales) to
+  // LDS buffer `scale_sb` before the barrier, so they are visible after it.
+  auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb) {
     __builtin_amdgcn_sched_barrier(0);
-    mma_half(fw[0], fa[0], swv, sav);
+    mma_half(fw[0], fa[0], swv, sav, first);
     read_half(cur, ch10, ch11, fw[1], fa[1]);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -612,6 +612,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitAll);
+    if constexpr (decltype(with_scales)::value) {
+      store_scales(scale_sb);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+    }
     __builtin_amdgcn_s_barrier();
   };
   auto back = [&](uint8_t* cur, const uint8_t* nxt, int dma_kb, int rs_kb, int rs_kb0, int rs_sb) {
@@ -621,7 +625,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     uint32_t swv1, sav1;
     read_scales(rs_kb, rs_kb0, rs_sb, swv1, sav1);
     issue(cur, dma_kb);
-    mma_half(fw[1], fa[1], swv, sav);
+    mma_half(fw[1], fa[1], swv, sav, std::false_type{});
     read_half(nxt, ch00, ch01, fw[0], fa[0]);
     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the two scale reads
 #pragma unroll
@@ -654,16 +658,17 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   __builtin_amdgcn_s_barrier();
   read_scales(0, ckb0, 0, swv, sav);
   read_half(st0, ch00, ch01, fw[0], fa[0]);
-  zero_acc();
 
+  const std::true_type yes{};
+  const std::false_type no{};
   for (int r = 0;; ++r) {
-    front(st0);                                  // stage 0 (first half)
+    front(st0, yes, no, 0);                      // stage 0 (first half): starts the sums
     int kb = 0;
     for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
       back(st0, st1, kb + 2, kb + 1, ckb0, csb);
-      front(st1);
+      front(st1, no, no, 0);
       back(st1, st0, kb + 3, kb + 2, ckb0, csb);
-      front(st0);
+      front(st0, no, no, 0);
     }
     // stages KB-2 (begun) and KB-1 remain; fetch the next tile meanwhile
     int ng, nt0, nn0, nkb0;
@@ -677,10 +682,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     set_dma_tile(ng, nt0, nn0, nkb0);
     load_scales(ng, nt0, nn0);
     back(st0, st1, 0, KB - 1, ckb0, csb);        // next tile's stage 0 -> st0
-    front(st1);                                  // waits for it and for the scale loads
-    store_scales(csb ^ 1);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
-    __builtin_amdgcn_s_barrier();
+    front(st1, no, yes, csb ^ 1);                // waits for it and for the scale loads; stages the scales
     back(st1, st0, 1, 0, nkb0, csb ^ 1);         // next tile's stage 1 -> st1; its stage 0 half 0
 
     // epilogue of this tile, straight from the accumulators (see bmm_large_kernel)
@@ -704,7 +706,6 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
       }
     }
     if (!more) break;
-    zero_acc();
     cg = ng;
     ct0 = nt0;
     cn0 = nn0;
