@@ -9,6 +9,12 @@
   weight once when dot_scaled cannot be used", Purpose): w_bf16[n, k] =
   bf16(decode(w[n,k]) * 2**(s[n, k/block] - 127)), rounded to nearest even
   from the exact fp64 product.
+* The BF16 arm of ``wo_a`` ("[ROCm][DSV4][Perf] Use FP8 WO_A output
+  projection", Summary and Related work: the path the FP8 one replaces and
+  keeps as its fallback -- an inverse RoPE, then a BF16 grouped einsum over a
+  BF16 copy of the weight made once at load): out[t, g, n] = sum_k
+  x[t,g,k] * W[g,n,k] on BF16 operands, in fp64, unrounded.  The BF16 weight
+  is the group-128 dequantisation of the FP8 checkpoint weight.
 * The MXFP8 linear (same page, Purpose and review thread): when K % 128 != 0
   the weight is used as BF16 (dequantised once at load, or per call when it
   was not prepared) and x stays BF16; when K % 128 == 0 the block-scaled FP8
@@ -19,6 +25,7 @@ import numpy as np
 
 from .formats import bf16_to_f64, e4m3_decode, e8m0_decode, f64_to_bf16_rne, OCP
 from .quant import group_quant
+from .rope import INTERLEAVED, inverse_rope
 
 #: The alignment that decides the MXFP8 linear's branch ("[ROCm][DSv4.1][Perf]
 #: Dequantize ...", Purpose: dot_scaled needs K % 128 == 0).
@@ -48,6 +55,27 @@ def bmm_a8w8_mxscale(a, a_scale, w, w_scale, a_fmt=OCP, block=128):
         wf = scaled_operand(w[g], w_scale[g], block, OCP)                  # [N, K]
         out[:, g, :] = af @ wf.T
     return out
+
+
+def bmm_bf16(x_bits, w_bits):
+    """x BF16 bits [T,G,K], W BF16 bits [G,N,K] -> out fp64 [T,G,N] (unrounded)."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    T, G, K = x_bits.shape
+    Gw, N, Kw = w_bits.shape
+    assert (Gw, Kw) == (G, K)
+    out = np.empty((T, G, N), dtype=np.float64)
+    for g in range(G):
+        out[:, g, :] = bf16_to_f64(x_bits[:, g, :]) @ bf16_to_f64(w_bits[g]).T
+    return out
+
+
+def wo_a_bf16(x_bits, positions, cos_bits, sin_bits, H, D, rope_dim, w_bits, style=INTERLEAVED):
+    """The BF16 arm end to end: inverse RoPE of x [T, H*D] to BF16, viewed as
+    [T, G, K], times the BF16 weight [G, N, K] -> fp64 [T, G, N]."""
+    G, _, K = np.asarray(w_bits).shape
+    xr = inverse_rope(x_bits, positions, cos_bits, sin_bits, H, D, rope_dim, style)
+    return bmm_bf16(xr.reshape(xr.shape[0], G, K), w_bits)
 
 
 def dequant_mxfp8_to_bf16(w, w_scale, block=32):

@@ -10,6 +10,11 @@
   BF16 (a library routine); it is exact for the scale range in use.
 * The MXFP8 linear's branch table as printed on the pages, and both branches
   on small inputs against exact evaluation.
+* The BF16 arm: the grouped BF16 product against exact rational sums (BF16
+  decoded by torch), a one-hot W per (g, n), equality with the FP8 product of
+  the group-128 dequantised operands; the end-to-end BF16 arm reduces to the
+  plain product at position 0 and lies within the FP8 quantisation error
+  bound of the FP8 arm.
 """
 
 from fractions import Fraction
@@ -148,3 +153,86 @@ def test_mx_linear_both_branches_exact(K):
         for n in range(4):
             ex = float(_exact_dot(xv[m], wv[n]))
             assert abs(out[m, n] - ex) <= 1e-12 * max(1.0, abs(ex))
+
+
+# ---- the BF16 arm: bmm_bf16 and wo_a_bf16
+
+
+def _torch_bf16_values(bits):
+    """BF16 bit patterns -> float64 through torch's own BF16 decode."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).view(torch.bfloat16)
+    return t.to(torch.float64).numpy()
+
+
+def test_bmm_bf16_against_exact_rationals():
+    rng = np.random.default_rng(11)
+    T, G, N, K = 3, 2, 5, 40
+    x = workloads.activations(rng, T * G, K).reshape(T, G, K)
+    w = workloads.activations(rng, G * N, K).reshape(G, N, K)
+    out = Gm.bmm_bf16(x, w)
+    xv, wv = _torch_bf16_values(x), _torch_bf16_values(w)
+    for t in range(T):
+        for g in range(G):
+            for n in range(N):
+                exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(xv[t, g], wv[g, n]))
+                mag = float(np.sum(np.abs(xv[t, g] * wv[g, n])))
+                assert abs(Fraction(out[t, g, n]) - exact) <= Fraction(K * mag) * Fraction(2) ** -52
+
+
+def test_bmm_bf16_one_hot_and_orientation():
+    rng = np.random.default_rng(12)
+    T, G, N, K = 4, 3, 6, 64
+    x = workloads.activations(rng, T * G, K).reshape(T, G, K)
+    w = np.zeros((G, N, K), np.uint16)
+    picks = (np.arange(N)[None, :] * 11 + 7 * np.arange(G)[:, None] + 5) % K     # per (g, n)
+    for g in range(G):
+        for n in range(N):
+            w[g, n, picks[g, n]] = 0x3F80       # BF16 1.0
+    out = Gm.bmm_bf16(x, w)
+    xv = _torch_bf16_values(x)
+    for g in range(G):
+        for n in range(N):
+            assert np.array_equal(out[:, g, n], xv[:, g, picks[g, n]])
+
+
+def test_bmm_bf16_equals_fp8_product_of_dequantised_operands():
+    # every scaled e4m3 value with scale exponents in [-12, -2] is a BF16 value,
+    # so the group-128 dequantisations carry the FP8 operands exactly and the two
+    # grouped products are the same fp64 computation
+    T, G, N, K = 5, 2, 7, 256
+    a, sa, w, sw = workloads.gemm_operands(13, T, G, N, K)
+    ab = Gm.dequant_mxfp8_to_bf16(a.reshape(T * G, K), sa.reshape(T * G, K // 128), 128).reshape(T, G, K)
+    wb = Gm.dequant_mxfp8_to_bf16(w.reshape(G * N, K), sw.reshape(G * N, K // 128), 128).reshape(G, N, K)
+    assert np.array_equal(Gm.bmm_bf16(ab, wb), Gm.bmm_a8w8_mxscale(a, sa, w, sw))
+
+
+def test_wo_a_bf16_position_zero_is_the_plain_product():
+    p = workloads.tiny()
+    cos, sin = workloads.rope_tables(rows=64)
+    wb = workloads.activations(np.random.default_rng(14), p.G * p.N, p.K).reshape(p.G, p.N, p.K)
+    zero = np.zeros(p.T, np.int64)
+    out = Gm.wo_a_bf16(p.x, zero, cos, sin, p.H, p.D, 64, wb)
+    assert np.array_equal(out, Gm.bmm_bf16(p.x.reshape(p.T, p.G, p.K), wb))
+
+
+def test_wo_a_bf16_within_fp8_quantisation_error_of_the_fp8_arm():
+    # The FP8 arm differs from the BF16 arm only by the activation quantisation:
+    # |q(r) - r| <= 2^-4 |r| + 2^(e-10) per element (e4m3 round to nearest,
+    # subnormal step 2^(e-9) with the group exponent e), so the two outputs
+    # differ by at most sum_k (2^-4 |r_k| + 2^(e_k-10)) |w_k|.
+    from oracle.quant import inv_rope_group_quant
+    from oracle.rope import inverse_rope
+    p = workloads.tiny()
+    cos, sin = workloads.rope_tables(rows=64)
+    wb = Gm.dequant_mxfp8_to_bf16(p.w.reshape(p.G * p.N, p.K), p.w_scale.reshape(p.G * p.N, -1), 128)
+    wb = wb.reshape(p.G, p.N, p.K)
+    bf = Gm.wo_a_bf16(p.x, p.positions, cos, sin, p.H, p.D, 64, wb)
+    q, s = inv_rope_group_quant(p.x, p.positions, cos, sin, p.H, p.D, 64)
+    fp8 = Gm.bmm_a8w8_mxscale(q.reshape(p.T, p.G, p.K), s.reshape(p.T, p.G, -1), p.w, p.w_scale)
+    r = _torch_bf16_values(inverse_rope(p.x, p.positions, cos, sin, p.H, p.D, 64)).reshape(p.T, p.G, p.K)
+    e = np.repeat(s.reshape(p.T, p.G, -1).astype(np.int64) - 127, 128, axis=2)
+    per = 2.0 ** -4 * np.abs(r) + np.ldexp(1.0, e - 10)
+    wv = np.abs(_torch_bf16_values(wb))
+    bound = np.einsum("tgk,gnk->tgn", per, wv)
+    assert np.all(np.abs(fp8 - bf) <= bound)
+    assert np.any(fp8 != bf)                   # the arms do differ
