@@ -86,9 +86,10 @@ void mx_set_dry_run(int on);
 
 /* Launch counters, in this order: quant, bmm (large tiles), bmm (small T),
  * dequant, linear BF16 branch (prepared weight), linear FP8 branch, linear
- * per-call-dequant branch, f32->e8m0 device, e4m3 encode device.  `out` gets
+ * per-call-dequant branch, f32->e8m0 device, e4m3 encode device, inverse RoPE
+ * to BF16, BF16 bmm (large tiles), BF16 bmm (small T).  `out` gets
  * min(n, MX_NUM_COUNTERS) values; returns MX_NUM_COUNTERS. */
-#define MX_NUM_COUNTERS 9
+#define MX_NUM_COUNTERS 12
 int mx_get_counters(uint64_t* out, int n);
 void mx_reset_counters(void);
 
@@ -144,6 +145,46 @@ mx_status mx_inv_rope_group_quant(const void* x, const int64_t* positions,
 mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t a_fmt,
                               const uint8_t* w, const uint8_t* w_scale, void* out,
                               int64_t T, int32_t G, int32_t N, int32_t K, void* stream);
+
+/* ------------------------------------------------ BF16 arm of wo_a */
+
+/*
+ * mx_inv_rope_bf16 -- inverse RoPE to BF16, the first step of the BF16 wo_a
+ * path that the FP8 one replaces and keeps as its fallback ([WOA], Summary
+ * and Related work: an inverse RoPE, then a BF16 grouped einsum over a BF16
+ * copy of the weight).
+ *
+ * out = x with the last rope_dim dims of every head rotated exactly as in
+ * mx_inv_rope_group_quant (same pairs, same fp32 arithmetic, BF16 nearest
+ * even); the other dims are copied.
+ * x, positions, cos, sin, max_pos, T, H, D, rope_dim, rope_style: as for
+ *           mx_inv_rope_group_quant.  A token whose position is outside
+ *           [0, max_pos) gets BF16 NaN (0x7FC0) in its rotated dims.
+ * out       device BF16 [T, H*D].  out == x runs in place, reading and
+ *           writing only the rotated dims (rope_dim/D of the tensor); any
+ *           other overlap of out and x is rejected.
+ * Requires: T >= 0 (0 is a no-op), H, D > 0, D % 8 == 0, rope_dim % 16 == 0,
+ * rope_dim <= D, x and out 16-byte aligned, cos/sin 16-byte aligned,
+ * positions 8-byte aligned, max_pos >= 1 when rope_dim > 0 and T > 0.
+ */
+mx_status mx_inv_rope_bf16(const void* x, const int64_t* positions, const void* cos,
+                           const void* sin, int64_t max_pos, int64_t T, int32_t H, int32_t D,
+                           int32_t rope_dim, int32_t rope_style, void* out, void* stream);
+
+/*
+ * mx_bmm_bf16 -- batched BF16 GEMM, the grouped einsum of the BF16 wo_a path
+ * ([WOA], Summary and Related work).
+ *
+ * out[t,g,n] = bf16( sum_k x[t,g,k] * W[g,n,k] ), fp32 accumulation, nearest even.
+ * x    device BF16 [T, G, K] (the rotated activation viewed per group).
+ * w    device BF16 [G, N, K] (e.g. the FP8 weight dequantised once with
+ *      mx_dequant_mxfp8_to_bf16 over [G*N, K] rows, block 128).
+ * out  device BF16 [T, G, N].
+ * Requires: T >= 0 (0 is a no-op), G >= 1, N >= 1 with N % 16 == 0, K >= 128
+ * with K % 128 == 0, 512*G*K < 2^32, x, w and out 16-byte aligned.
+ */
+mx_status mx_bmm_bf16(const void* x, const void* w, void* out, int64_t T, int32_t G,
+                      int32_t N, int32_t K, void* stream);
 
 /* ------------------------------------------------------- MXFP8 linear */
 

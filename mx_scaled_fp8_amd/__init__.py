@@ -23,6 +23,7 @@ __all__ = [
     "mx_probe", "mx_version", "mx_set_dry_run", "mx_get_counters", "mx_reset_counters",
     "mx_inv_rope_group_quant", "mx_bmm_a8w8_mxscale", "mx_dequant_mxfp8_to_bf16",
     "mx_linear_dequant_at_load", "mx_linear_workspace_bytes", "mx_linear",
+    "mx_inv_rope_bf16", "mx_bmm_bf16",
     "mx_f32_pow2_to_e8m0", "mx_f32_pow2_to_e8m0_device", "mx_f32_to_e4m3_ocp",
     "mx_f32_to_e4m3_fnuz", "mx_f32_to_e4m3_device", "mx_e4m3_to_f32", "mx_e8m0_to_f32",
     "COUNTER_NAMES",
@@ -34,7 +35,8 @@ MX_ROPE_INTERLEAVED, MX_ROPE_NEOX = 0, 1
 MX_LINEAR_K_ALIGN = 128
 MX_LINEAR_BLOCK = 32
 COUNTER_NAMES = ("quant", "bmm_large", "bmm_small", "dequant", "linear_bf16", "linear_fp8",
-                 "linear_percall_dequant", "f32_to_e8m0_device", "f32_to_e4m3_device")
+                 "linear_percall_dequant", "f32_to_e8m0_device", "f32_to_e4m3_device", "rope_bf16",
+                 "bmm_bf16_large", "bmm_bf16_small")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
@@ -70,6 +72,8 @@ def lib():
             "mx_inv_rope_group_quant": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, I32, I32, I32, P, P, P]),
             "mx_bmm_a8w8_mxscale": (ctypes.c_int, [P, P, I32, P, P, P, I64, I32, I32, I32, P]),
             "mx_dequant_mxfp8_to_bf16": (ctypes.c_int, [P, P, P, I64, I64, I32, P]),
+            "mx_inv_rope_bf16": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, I32, P, P]),
+            "mx_bmm_bf16": (ctypes.c_int, [P, P, P, I64, I32, I32, I32, P]),
             "mx_linear_dequant_at_load": (ctypes.c_int, [I64]),
             "mx_linear_workspace_bytes": (SZ, [I64, I64, I64, I32]),
             "mx_linear": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P, SZ, P]),
@@ -169,6 +173,31 @@ def mx_bmm_a8w8_mxscale(a, a_scale, w, w_scale, a_fmt=MX_FP8_E4M3_OCP, out=None)
         out = torch.empty((T, G, N), dtype=torch.bfloat16, device=a.device)
     _check(lib().mx_bmm_a8w8_mxscale(_dev(a, "a", 1), _dev(a_scale, "a_scale", 1), a_fmt, _dev(w, "w", 1),
                                      _dev(w_scale, "w_scale", 1), _dev(out, "out", 2), T, G, N, K, _stream(a)))
+    return out
+
+
+# ------------------------------------------------------- BF16 arm of wo_a
+
+def mx_inv_rope_bf16(x, positions, cos, sin, H, D, rope_dim, rope_style=MX_ROPE_INTERLEAVED, out=None):
+    """x BF16 [T, H*D] -> rotated BF16 [T, H*D]; ``out=x`` rotates in place."""
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, H * D), dtype=x.dtype, device=x.device)
+    max_pos = cos.shape[0] if cos is not None else 0
+    _check(lib().mx_inv_rope_bf16(
+        _dev(x, "x", 2), _dev(positions, "positions", 8) if positions is not None else None,
+        _dev(cos, "cos", 2) if cos is not None else None, _dev(sin, "sin", 2) if sin is not None else None,
+        max_pos, T, H, D, rope_dim, rope_style, _dev(out, "out", 2), _stream(x)))
+    return out
+
+
+def mx_bmm_bf16(x, w, out=None):
+    """x BF16 [T,G,K], w BF16 [G,N,K] -> BF16 [T,G,N]."""
+    T, G, K = x.shape
+    N = w.shape[1]
+    if out is None:
+        out = torch.empty((T, G, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().mx_bmm_bf16(_dev(x, "x", 2), _dev(w, "w", 2), _dev(out, "out", 2), T, G, N, K, _stream(x)))
     return out
 
 

@@ -26,6 +26,11 @@ mx_status launch_dequant(const uint8_t* w, const uint8_t* w_scale, void* out, in
                          hipStream_t stream);
 mx_status launch_f32_to_e8m0(const float* in, uint8_t* out, int64_t n, int32_t* reject_count, hipStream_t stream);
 mx_status launch_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, int32_t fmt, hipStream_t stream);
+mx_status launch_rope_bf16(const void* x, const int64_t* positions, const void* cos, const void* sin,
+                           int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
+                           void* out, hipStream_t stream);
+mx_status launch_bmm_bf16(const void* x, const void* w, void* out, int64_t T, int32_t G, int32_t N, int32_t K,
+                          hipStream_t stream);
 
 namespace {
 
@@ -209,6 +214,58 @@ mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t 
   MX_CHECK(aligned(out, 16), "%s: out must be 16-byte aligned", fn);
   MX_PREAMBLE();
   const mx_status st = launch_bmm(a, a_scale, a_fmt, w, w_scale, out, T, G, N, K, static_cast<hipStream_t>(stream));
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_inv_rope_bf16(const void* x, const int64_t* positions, const void* cos, const void* sin,
+                           int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t rope_style,
+                           void* out, void* stream) {
+  const char* fn = "mx_inv_rope_bf16";
+  MX_CHECK(T >= 0, "%s: T = %lld < 0", fn, (long long)T);
+  MX_CHECK(H > 0 && D > 0, "%s: H = %d and D = %d must be positive", fn, H, D);
+  MX_CHECK(D % 8 == 0, "%s: D = %d must be a multiple of 8", fn, D);
+  const int64_t L = static_cast<int64_t>(H) * D;
+  MX_CHECK(L / 8 < (int64_t(1) << 30), "%s: H*D = %lld is too large", fn, (long long)L);
+  MX_CHECK(rope_dim >= 0 && rope_dim <= D && rope_dim % 16 == 0, "%s: rope_dim = %d (multiple of 16, <= D = %d)",
+           fn, rope_dim, D);
+  MX_CHECK(rope_style == MX_ROPE_INTERLEAVED || rope_style == MX_ROPE_NEOX, "%s: unknown rope style %d", fn,
+           rope_style);
+  if (T == 0) { clear_error(); return MX_OK; }
+  MX_CHECK(x && out, "%s: null tensor pointer", fn);
+  MX_CHECK(aligned(x, 16) && aligned(out, 16), "%s: x and out must be 16-byte aligned", fn);
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), ob = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t bytes = static_cast<uintptr_t>(T * L * 2);
+  MX_CHECK(xb == ob || xb + bytes <= ob || ob + bytes <= xb, "%s: out overlaps x without being x", fn);
+  if (rope_dim > 0) {
+    MX_CHECK(positions && cos && sin, "%s: rope_dim > 0 needs positions, cos and sin", fn);
+    MX_CHECK(max_pos >= 1, "%s: max_pos = %lld", fn, (long long)max_pos);
+    MX_CHECK(aligned(cos, 16) && aligned(sin, 16) && aligned(positions, 8),
+             "%s: cos/sin must be 16-byte aligned, positions 8-byte aligned", fn);
+  }
+  MX_PREAMBLE();
+  count(C_ROPE_BF16);
+  const mx_status st = launch_rope_bf16(x, positions, cos, sin, max_pos, T, H, D, rope_dim, rope_style, out,
+                                        static_cast<hipStream_t>(stream));
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_bmm_bf16(const void* x, const void* w, void* out, int64_t T, int32_t G, int32_t N, int32_t K,
+                      void* stream) {
+  const char* fn = "mx_bmm_bf16";
+  MX_CHECK(T >= 0 && T < (int64_t(1) << 31), "%s: T = %lld out of range", fn, (long long)T);
+  MX_CHECK(G >= 1 && N >= 1 && K >= 1, "%s: G = %d, N = %d, K = %d must be positive", fn, G, N, K);
+  MX_CHECK(K % 128 == 0, "%s: K = %d is not a multiple of 128", fn, K);
+  MX_CHECK(N % 16 == 0, "%s: N = %d is not a multiple of 16", fn, N);
+  MX_CHECK(static_cast<int64_t>(256) * G * K * 2 < (int64_t(1) << 32) &&
+               static_cast<int64_t>(N) * K < (int64_t(1) << 31),
+           "%s: G*K or N*K too large for 32-bit tile offsets", fn);
+  if (T == 0) { clear_error(); return MX_OK; }
+  MX_CHECK(x && w && out, "%s: null tensor pointer", fn);
+  MX_CHECK(aligned(x, 16) && aligned(w, 16) && aligned(out, 16), "%s: x, w and out must be 16-byte aligned", fn);
+  MX_PREAMBLE();
+  const mx_status st = launch_bmm_bf16(x, w, out, T, G, N, K, static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();
   return st;
 }

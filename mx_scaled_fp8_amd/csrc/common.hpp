@@ -34,6 +34,9 @@ enum Counter {
   C_LINEAR_PERCALL,
   C_E8M0_DEVICE,
   C_E4M3_DEVICE,
+  C_ROPE_BF16,
+  C_BMM_BF16_LARGE,
+  C_BMM_BF16_SMALL,
 };
 void count(Counter c);
 

@@ -11,6 +11,10 @@
 // partial sums through LDS.  The weight is the MFMA's first operand, so each
 // lane ends with four consecutive n of one row (one 8-byte store).  K only
 // has to be a multiple of 32 (288 and 576 are not multiples of 128).
+//
+// The same kernel runs the decode batch of the BF16 wo_a arm: G independent
+// products x[:, g, :] * W[g]^T with x rows G*K apart and out rows G*N apart,
+// one grid layer per group.
 #include "common.hpp"
 
 namespace mx {
@@ -29,10 +33,14 @@ __device__ __forceinline__ v8bf as_v8bf(const uint4 v) {
 template <int NT>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
                                                         uint16_t* __restrict__ out, int M, int N, int K,
-                                                        int n_groups) {
+                                                        int n_groups, int64_t ldx, int64_t ldo) {
   __shared__ float red[4][NT * 4][4][64];
   const int n0 = (blockIdx.x % n_groups) * (16 * NT);
   const int m0 = blockIdx.y * 64;
+  const int g = blockIdx.z;                 // group: x + g*K, W + g*N*K, out + g*N
+  x += static_cast<size_t>(g) * K;
+  w += static_cast<size_t>(g) * N * K;
+  out += static_cast<size_t>(g) * N;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int KS = K / 32;
@@ -43,7 +51,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   for (int i = 0; i < NT; ++i) pw[i] = w + static_cast<size_t>(min(n0 + i * 16 + (lane & 15), N - 1)) * K + kq;
   const uint16_t* px[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) px[j] = x + static_cast<size_t>(min(m0 + j * 16 + (lane & 15), M - 1)) * K + kq;
+  for (int j = 0; j < 4; ++j) px[j] = x + static_cast<size_t>(min(m0 + j * 16 + (lane & 15), M - 1)) * ldx + kq;
 
   v4f acc[NT][4];
 #pragma unroll
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
     const int m = m0 + j * 16 + (lane & 15);
     const int n = n0 + i * 16 + (lane >> 4) * 4;
     if (m < M && n < N)
-      *reinterpret_cast<uint2*>(out + static_cast<size_t>(m) * N + n) =
+      *reinterpret_cast<uint2*>(out + static_cast<size_t>(m) * ldo + n) =
           make_uint2(pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3]));
   }
 }
@@ -94,8 +102,21 @@ mx_status launch_gemm_bf16(const void* x, const void* w, void* out, int64_t M, i
   const dim3 grid(n_groups, static_cast<unsigned>((M + 63) / 64));
   gemm_bf16_kernel<1><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
                                                  static_cast<uint16_t*>(out), static_cast<int>(M),
-                                                 static_cast<int>(N), static_cast<int>(K), n_groups);
+                                                 static_cast<int>(N), static_cast<int>(K), n_groups, K, N);
   return launch_status("mx_linear (BF16 GEMM)");
+}
+
+// G products out[:, g, :] = x[:, g, :] * W[g]^T with row strides ldx (x) and
+// ldo (out) in elements; 32 columns per workgroup (N % 16 == 0, K % 32 == 0).
+mx_status launch_gemm_bf16_strided(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K,
+                                   int32_t G, int64_t ldx, int64_t ldo, hipStream_t stream) {
+  if (M == 0 || N == 0) return MX_OK;
+  const int n_groups = static_cast<int>((N + 31) / 32);
+  const dim3 grid(n_groups, static_cast<unsigned>((M + 63) / 64), static_cast<unsigned>(G));
+  gemm_bf16_kernel<2><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                                                 static_cast<uint16_t*>(out), static_cast<int>(M),
+                                                 static_cast<int>(N), static_cast<int>(K), n_groups, ldx, ldo);
+  return launch_status("mx_bmm_bf16 (small T)");
 }
 
 }  // namespace mx

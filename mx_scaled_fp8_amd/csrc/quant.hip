@@ -260,6 +260,113 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- BF16 arm
+//
+// Inverse RoPE to BF16 with no quantisation: the first half of the BF16 wo_a
+// path ("[ROCm][DSV4][Perf] Use FP8 WO_A output projection", Summary and
+// Related work: an inverse RoPE followed by a BF16 grouped einsum, kept as
+// the fallback).  Same rotation arithmetic as the quantiser.  The unit of
+// work is 8 rotated pairs = 16 BF16 held in two 16-byte chunks (interleaved:
+// two consecutive chunks; split halves: a chunk of first components and the
+// chunk of their partners rope_dim/2 dims on), so a lane owns both members
+// of each of its pairs and the pass can run in place.
+//
+//  * in place (out == x): one lane per unit; only the rotated slice of each
+//    head is read and written (rope_dim/D of the tensor);
+//  * out of place: one lane per 8-element chunk of the whole tensor; chunks
+//    outside the rotated slice are copied, the first chunk of a unit
+//    rotates the unit, the second is left to it.
+// A token whose position is outside [0, max_pos) gets BF16 NaN (0x7FC0) in
+// its rotated dims; the other dims pass through.
+
+struct RopeArgs {
+  const uint4* x;             // [T, L] BF16 as 16-byte chunks
+  uint4* out;                 // [T, L]
+  const int64_t* pos;         // [T]
+  const uint16_t* cos;        // [max_pos, R/2]
+  const uint16_t* sin;
+  int64_t max_pos;
+  uint32_t total;             // units (in place) or chunks (out of place) of this launch
+  DivU32 row_div;             // units per row (H * R/16) or chunks per row (L/8)
+  DivU32 head_div;            // units per head (R/16) or chunks per head (D/8)
+  uint32_t head_chunks;       // D / 8
+  uint32_t row_chunks;        // L / 8
+  uint32_t rope_chunk0;       // (D - R) / 8
+  uint32_t half_pairs;        // R / 2
+};
+
+// Rotates unit u of head slice starting at chunk `c0` (the head's first
+// rotated chunk) of row `row`, reading from x and writing to out.
+template <int STYLE>
+__device__ __forceinline__ void rope_unit_bf16(const RopeArgs& a, uint32_t row, uint32_t c0, uint32_t u) {
+  const uint32_t ca = c0 + (STYLE == MX_ROPE_INTERLEAVED ? 2 * u : u);
+  const uint32_t cb = ca + (STYLE == MX_ROPE_INTERLEAVED ? 1 : a.half_pairs / 8);
+  const uint4 va = a.x[ca], vb = a.x[cb];
+  const int64_t p = a.pos[row];
+  if (p < 0 || p >= a.max_pos) {
+    const uint4 nan = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+    a.out[ca] = nan;
+    a.out[cb] = nan;
+    return;
+  }
+  const uint4 cc = *reinterpret_cast<const uint4*>(a.cos + p * a.half_pairs + 8 * u);
+  const uint4 ss = *reinterpret_cast<const uint4*>(a.sin + p * a.half_pairs + 8 * u);
+  const uint32_t cw[4] = {cc.x, cc.y, cc.z, cc.w};
+  const uint32_t sw[4] = {ss.x, ss.y, ss.z, ss.w};
+  uint32_t wa[4] = {va.x, va.y, va.z, va.w};
+  uint32_t wb[4] = {vb.x, vb.y, vb.z, vb.w};
+  if constexpr (STYLE == MX_ROPE_INTERLEAVED) {
+    // dword k of the unit is pair k: (x, y) = (lo, hi)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float xr, yr;
+      inv_rotate(bf16_lo(wa[k]), bf16_hi(wa[k]), bf16_lo(k & 1 ? cw[k >> 1] >> 16 : cw[k >> 1]),
+                 bf16_lo(k & 1 ? sw[k >> 1] >> 16 : sw[k >> 1]), xr, yr);
+      wa[k] = pk_bf16(xr, yr);
+      inv_rotate(bf16_lo(wb[k]), bf16_hi(wb[k]), bf16_lo(k & 1 ? cw[2 + (k >> 1)] >> 16 : cw[2 + (k >> 1)]),
+                 bf16_lo(k & 1 ? sw[2 + (k >> 1)] >> 16 : sw[2 + (k >> 1)]), xr, yr);
+      wb[k] = pk_bf16(xr, yr);
+    }
+  } else {
+    // element e of chunk a is the first component of pair e, of chunk b the second
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float x0, y0, x1, y1;
+      inv_rotate(bf16_lo(wa[k]), bf16_lo(wb[k]), bf16_lo(cw[k]), bf16_lo(sw[k]), x0, y0);
+      inv_rotate(bf16_hi(wa[k]), bf16_hi(wb[k]), bf16_hi(cw[k]), bf16_hi(sw[k]), x1, y1);
+      wa[k] = pk_bf16(x0, x1);
+      wb[k] = pk_bf16(y0, y1);
+    }
+  }
+  a.out[ca] = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+  a.out[cb] = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+}
+
+template <int STYLE, bool COPY>
+__global__ __launch_bounds__(kThreads) void rope_bf16_kernel(RopeArgs a) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.total) return;
+  const uint32_t row = div_u32(i, a.row_div);
+  const uint32_t rem = i - row * a.row_div.d;
+  const uint32_t head = div_u32(rem, a.head_div);
+  const uint32_t hin = rem - head * a.head_div.d;
+  const uint32_t c0 = row * a.row_chunks + head * a.head_chunks + a.rope_chunk0;
+  if constexpr (!COPY) {
+    rope_unit_bf16<STYLE>(a, row, c0, hin);
+  } else {
+    if (hin < a.rope_chunk0) {
+      a.out[i] = a.x[i];
+      return;
+    }
+    const uint32_t s = hin - a.rope_chunk0;      // chunk inside the rotated slice
+    if (STYLE == MX_ROPE_INTERLEAVED) {
+      if ((s & 1) == 0) rope_unit_bf16<STYLE>(a, row, c0, s >> 1);
+    } else {
+      if (s < a.half_pairs / 8) rope_unit_bf16<STYLE>(a, row, c0, s);
+    }
+  }
+}
+
 template <int GROUP, int FMT>
 void launch_style(const QuantArgs& a, bool rope, int style, uint32_t blocks, hipStream_t s) {
   if (!rope)
@@ -315,6 +422,51 @@ mx_status launch_quant(const void* x, const int64_t* positions, const void* cos,
       else launch_style<32, MX_FP8_E4M3_FNUZ>(a, rope, style, blocks, stream);
     }
     const mx_status st = launch_status("mx_inv_rope_group_quant");
+    if (st != MX_OK) return st;
+  }
+  return MX_OK;
+}
+
+
+// Inverse RoPE to BF16 over rows [0, T) (arguments validated by the caller;
+// out == x runs in place).
+mx_status launch_rope_bf16(const void* x, const int64_t* positions, const void* cos, const void* sin,
+                           int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
+                           void* out, hipStream_t stream) {
+  const int64_t L = static_cast<int64_t>(H) * D;
+  const bool in_place = out == x;
+  if (rope_dim == 0 && in_place) return MX_OK;
+  const int64_t per_row = in_place ? static_cast<int64_t>(H) * (rope_dim / 16) : L / 8;
+  const int64_t max_rows = std::max<int64_t>(1, (int64_t(1) << 31) / std::max<int64_t>(L / 8, 1) - 1);
+  for (int64_t r0 = 0; r0 < T; r0 += max_rows) {
+    const int64_t rows = std::min(max_rows, T - r0);
+    RopeArgs a;
+    a.x = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(x) + r0 * L);
+    a.out = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + r0 * L);
+    a.pos = positions ? positions + r0 : nullptr;
+    a.cos = static_cast<const uint16_t*>(cos);
+    a.sin = static_cast<const uint16_t*>(sin);
+    a.max_pos = max_pos;
+    a.total = static_cast<uint32_t>(rows * per_row);
+    a.row_div = make_div(static_cast<uint32_t>(per_row));
+    a.head_div = make_div(static_cast<uint32_t>(in_place ? rope_dim / 16 : D / 8));
+    a.head_chunks = static_cast<uint32_t>(D / 8);
+    a.row_chunks = static_cast<uint32_t>(L / 8);
+    a.rope_chunk0 = static_cast<uint32_t>((D - rope_dim) / 8);
+    a.half_pairs = static_cast<uint32_t>(rope_dim / 2);
+    const uint32_t blocks = (a.total + kThreads - 1) / kThreads;
+    if (rope_dim == 0) {
+      // nothing rotates: every chunk is copied (no position is read)
+      a.rope_chunk0 = a.head_chunks;
+      rope_bf16_kernel<MX_ROPE_INTERLEAVED, true><<<blocks, kThreads, 0, stream>>>(a);
+    } else if (style == MX_ROPE_INTERLEAVED) {
+      if (in_place) rope_bf16_kernel<MX_ROPE_INTERLEAVED, false><<<blocks, kThreads, 0, stream>>>(a);
+      else rope_bf16_kernel<MX_ROPE_INTERLEAVED, true><<<blocks, kThreads, 0, stream>>>(a);
+    } else {
+      if (in_place) rope_bf16_kernel<MX_ROPE_NEOX, false><<<blocks, kThreads, 0, stream>>>(a);
+      else rope_bf16_kernel<MX_ROPE_NEOX, true><<<blocks, kThreads, 0, stream>>>(a);
+    }
+    const mx_status st = launch_status("mx_inv_rope_bf16");
     if (st != MX_OK) return st;
   }
   return MX_OK;

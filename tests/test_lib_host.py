@@ -191,6 +191,41 @@ def test_linear_validation(dry):
     assert f(K=1152, M=65) == mx.MX_ERR_INVALID_ARG
 
 
+def _rope_bf16(**kw):
+    a = dict(x=FAKE, pos=FAKE, cos=FAKE, sin=FAKE, max_pos=100, T=16, H=4, D=128, R=64, style=0, out=FAKE * 4)
+    a.update(kw)
+    return _call("mx_inv_rope_bf16", a["x"], a["pos"], a["cos"], a["sin"], a["max_pos"], a["T"], a["H"], a["D"],
+                 a["R"], a["style"], a["out"], None)
+
+
+def test_rope_bf16_validation(dry):
+    assert _rope_bf16() == mx.MX_OK
+    assert _rope_bf16(out=FAKE) == mx.MX_OK                              # in place
+    assert _rope_bf16(T=0, x=None, out=None) == mx.MX_OK
+    assert _rope_bf16(R=0, pos=None, cos=None, sin=None) == mx.MX_OK     # a plain copy
+    # x spans 16 * 512 * 2 = 16 KiB: an out that starts inside it overlaps
+    for bad in (dict(T=-1), dict(H=0), dict(D=12), dict(R=72), dict(R=8), dict(R=256), dict(style=2),
+                dict(x=None), dict(out=None), dict(pos=None), dict(x=FAKE + 8), dict(out=FAKE * 4 + 8),
+                dict(max_pos=0), dict(cos=FAKE + 8), dict(out=FAKE + 4096), dict(x=FAKE * 4 + 1024)):
+        assert _rope_bf16(**bad) == mx.MX_ERR_INVALID_ARG, bad
+        assert mx.lib().mx_last_error().decode()
+    assert _rope_bf16(out=FAKE + 16 * 512 * 2) == mx.MX_OK              # adjacent, not overlapping
+
+
+def _bmm_bf16(**kw):
+    a = dict(x=FAKE, w=FAKE, out=FAKE, T=8192, G=16, N=1024, K=4096)
+    a.update(kw)
+    return _call("mx_bmm_bf16", a["x"], a["w"], a["out"], a["T"], a["G"], a["N"], a["K"], None)
+
+
+def test_bmm_bf16_validation(dry):
+    assert _bmm_bf16() == mx.MX_OK
+    assert _bmm_bf16(T=0, x=None) == mx.MX_OK
+    for bad in (dict(K=4000), dict(K=64), dict(N=100), dict(G=0), dict(T=-3), dict(x=None), dict(w=FAKE + 4),
+                dict(out=FAKE + 2), dict(G=2048, K=4096)):
+        assert _bmm_bf16(**bad) == mx.MX_ERR_INVALID_ARG, bad
+
+
 def test_converter_validation(dry):
     assert _call("mx_f32_to_e4m3_device", FAKE, FAKE, 10, 0, None) == mx.MX_OK
     assert _call("mx_f32_to_e4m3_device", FAKE, FAKE, 10, 5, None) == mx.MX_ERR_INVALID_ARG
