@@ -148,9 +148,9 @@ def cpu_baseline(workloads, tokens):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
-def bench_extra(mx, torch, workloads, reps=50):
+def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50):
     """Secondary per-kernel timings: decode batch (cold weights), MXFP8 linear,
-    dequantisation."""
+    dequantisation, the BF16 arm."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     tm = Timer(torch, stream)
@@ -226,6 +226,66 @@ def bench_extra(mx, torch, workloads, reps=50):
     res["dequant_5120x576"] = {"us": us_dq, "GBps": (5120 * 576 * 3 + 5120 * 18) / us_dq / 1e3,
                                "algorithmic_bytes": 5120 * 576 * 3 + 5120 * 18}
     res["graph_40_calls"] = bench_graphs(mx, torch, workloads)
+    res["bf16_arm"] = bench_bf16_arm(mx, torch, workloads, fp8_step_us, fp8_bmm_us)
+    return res
+
+
+def bench_bf16_arm(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=30):
+    """The BF16 wo_a arm (the path the FP8 one replaces): inverse RoPE to BF16,
+    then the batched BF16 GEMM on the weight dequantised once at load (block
+    128), on the same prefill chunk and decode batch; the FP8 arm's speedups
+    are ratios of per-launch times measured in this process."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    tm = Timer(torch, stream)
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    def timeit(fn, n=reps):
+        for _ in range(3):
+            fn(0)
+        ts = []
+        for i in range(n):
+            a = tm.event()
+            fn(i)
+            b = tm.event()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ts])) * 1e3
+
+    res = {}
+    for name, prob, rows, copies in (("prefill_T8192", workloads.prefill_chunk, 8192, 1),
+                                     ("decode_T64", workloads.decode_batch, 32768, 6)):
+        p = prob()
+        cos, sin = workloads.rope_tables(rows=rows)
+        x, cosd, sind = u16(p.x), u16(cos), u16(sin)
+        pos = torch.from_numpy(p.positions).to(dev)
+        w8 = torch.from_numpy(p.w.reshape(p.G * p.N, p.K)).to(dev)
+        ws8 = torch.from_numpy(p.w_scale.reshape(p.G * p.N, -1)).to(dev)
+        wb = [mx.mx_dequant_mxfp8_to_bf16(w8, ws8, block=128).view(p.G, p.N, p.K) for _ in range(copies)]
+        del w8, ws8
+        L = p.H * p.D
+        xr = torch.empty_like(x)
+        out = torch.empty((p.T, p.G, p.N), dtype=torch.bfloat16, device=dev)
+        us_copy = timeit(lambda i: mx.mx_inv_rope_bf16(x, pos, cosd, sind, p.H, p.D, 64, out=xr))
+        xi = x.clone()       # rotated in place again and again: same cost every time
+        us_inpl = timeit(lambda i: mx.mx_inv_rope_bf16(xi, pos, cosd, sind, p.H, p.D, 64, out=xi))
+        us_bmm = timeit(lambda i: mx.mx_bmm_bf16(xr.view(p.T, p.G, p.K), wb[i % copies], out=out))
+        rope_bytes_inpl = p.T * (p.H * 64 * 4 + 8 + 2 * 64)
+        rope_bytes_copy = p.T * (L * 4 + 8 + 2 * 64)
+        gemm_bytes = p.T * p.G * p.K * 2 + p.G * p.N * p.K * 2 + p.T * p.G * p.N * 2
+        res[name] = {
+            "rope_in_place_us": us_inpl, "rope_in_place_GBps": rope_bytes_inpl / us_inpl / 1e3,
+            "rope_copy_us": us_copy, "rope_copy_GBps": rope_bytes_copy / us_copy / 1e3,
+            "bmm_bf16_us": us_bmm, "bmm_bf16_TFLOPs": p.flops / us_bmm / 1e6,
+            "bmm_bf16_frac_bf16_peak": p.flops / us_bmm / 1e6 / PEAK_BF16_TFLOPS,
+            "bmm_bf16_GBps": gemm_bytes / us_bmm / 1e3,
+            "step_us": us_inpl + us_bmm,
+            "weights": "cold (6 rotating copies)" if copies > 1 else "resident",
+        }
+        if name == "prefill_T8192":
+            res[name]["fp8_speedup_bmm"] = us_bmm / fp8_bmm_us
+            res[name]["fp8_speedup_step"] = (us_inpl + us_bmm) / fp8_step_us
+        del x, xr, xi, out, wb
     return res
 
 
@@ -362,7 +422,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--extra", action="store_true", help="also time decode, MXFP8 linear, dequant")
+    ap.add_argument("--extra", action="store_true", help="also time decode, MXFP8 linear, dequant, the BF16 arm")
     ap.add_argument("--long", action="store_true", help="also time the 100,000-token chunked prefill")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 1 GiB device-to-device copies (the reference kernel for "
@@ -431,7 +491,7 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(workloads, args.cpu_tokens)
     if args.extra:
         log("[bench] secondary kernels")
-        rec["kernels"] = bench_extra(mx, torch, workloads)
+        rec["kernels"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3)
     if args.long:
         log("[bench] 100,000-token chunked prefill")
         rec["long_prefill_100k"] = bench_long(mx, torch, workloads)
