@@ -361,6 +361,41 @@ def bench_graphs(mx, torch, workloads, calls=40, replays=20):
         del copies, wprep
     out["mxfp8_linear_M64_N4096"] = lin
 
+    # the pages' production layer: the shared expert's down_proj, N = 5120, at
+    # each tensor-parallel share of K = 2304, decode batches of 1 and 8 rows;
+    # every branch the share allows, one weight per layer of a 40-layer stack
+    dp = {}
+    for tp, (xh, wh, wsh) in workloads.down_proj_shards().items():
+        N, K = wh.shape
+        wd, wsd = torch.from_numpy(wh).to(dev), torch.from_numpy(wsh).to(dev)
+        arms = {"fp8 block-scaled": wd} if K % 128 == 0 else {
+            "per-call dequant": wd, "dequant once": mx.mx_dequant_mxfp8_to_bf16(wd, wsd)}
+        for M in (1, 8):
+            xd = u16(xh[:M])
+            o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            for arm, wprep in arms.items():
+                copies = [(wprep.clone(), wsd.clone()) for _ in range(calls)]
+                wsp = torch.empty(max(1, mx.mx_linear_workspace_bytes(M, N, K, wprep.element_size())),
+                                  dtype=torch.uint8, device=dev)
+
+                def rec_dp():
+                    for w, sw in copies:
+                        mx.mx_linear(xd, w, sw, out=o, workspace=wsp)
+                us = time_graph(rec_dp)
+                io = M * K * 2 + M * N * 2
+                if arm == "per-call dequant":
+                    b = N * K + N * K // 32 + N * K * 2 + N * K * 2 + io      # dequant pass + BF16 GEMM
+                elif arm == "dequant once":
+                    b = N * K * 2 + io
+                else:
+                    b = N * K + N * K // 32 + io + 2 * (M * K + M * K // 32)   # x codes written, read back
+                dp[f"TP{tp}_K{K}_M{M}_{arm.replace(' ', '_')}"] = {
+                    "us_per_call": us, "us_per_token_40_layers": 40 * us, "bytes_per_call": b,
+                    "bytes_per_token_40_layers": 40 * b, "GBps": b / us / 1e3}
+                del copies
+        del arms, wd, wsd
+    out["down_proj_decode_N5120"] = dp
+
     # load-time dequantisation, the pages' 5120 x 576 weight, 40 layers
     rng = np.random.default_rng(21)
     wd = torch.from_numpy(workloads.weight_codes(rng, (5120, 576))).to(dev)

@@ -11,6 +11,9 @@
   and the launch counters show that the scaled GEMM was never reached (the
   review thread of the MXFP8 page asks for exactly these two checks).
 * The converter turns the FP32 power-of-two scales into the same E8M0 bytes.
+* The pages' production layer, the shared expert's down_proj (N = 5120) at
+  each tensor-parallel share of K = 2304 (TP1/2/4/8: K = 2304, 1152, 576,
+  288), decode batches of 1 and 8 rows: every branch the K allows.
 """
 
 import numpy as np
@@ -116,3 +119,27 @@ def test_linear_small_m(M):
         ws = workloads.scale_bytes(rng, (128, K // 32), -10, -4)
         out = host_u16(mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws)))
         assert_gemm_close(out, G.mx_linear(x, w, ws, 32), f"M={M} K={K}")
+
+
+@pytest.fixture(scope="module")
+def shards():
+    return workloads.down_proj_shards()
+
+
+@pytest.mark.parametrize("M", [1, 8])
+@pytest.mark.parametrize("tp", workloads.DOWN_PROJ_TP)
+def test_down_proj_production_shares(shards, tp, M):
+    x, w, ws = shards[tp]
+    x = x[:M]
+    K = w.shape[1]
+    dx, dw, dws = dev_u16(x), dev_u8(w), dev_u8(ws)
+    ref = G.mx_linear(x, w, ws, 32)
+    say("down_proj share", tp, K, M)
+    if K % 128:
+        once = host_u16(mx.mx_linear(dx, mx.mx_dequant_mxfp8_to_bf16(dw, dws), dws))
+        assert_gemm_close(once, ref, f"TP{tp} K={K} M={M} dequant once")
+        percall = host_u16(mx.mx_linear(dx, dw, dws))
+        assert np.array_equal(percall, once)
+    else:
+        out = host_u16(mx.mx_linear(dx, dw, dws))
+        assert_gemm_close(out, ref, f"TP{tp} K={K} M={M} fp8")

@@ -19,6 +19,10 @@ Draw order is part of the recipe (numpy ``default_rng``, PCG64):
 * MXFP8 linear (seed 3): for K in (288, 576, 1152, 2304) in that order: x
   (64, K) std normal; W codes (4096, K); scale exponents (4096, K/32) in
   [-10, -4].
+* shared-expert down_proj (seed 5): x (8, 2304) std normal; W codes
+  (5120, 2304); scale exponents (5120, 72) in [-10, -4].  The TP-P shard is
+  the first 2304/P columns of each (K = 2304, 1152, 576, 288 at TP1/2/4/8);
+  decode batches of 1 and 8 rows take the first rows of x.
 * long prefill (seed 4): outlier columns, W codes and scale exponents as the
   prefill chunk.  100,000 tokens = 12 chunks of 8192 + one of 1,696;
   positions 8192c + i.  Chunk c's activations are drawn on the GPU with
@@ -135,6 +139,26 @@ def mxfp8_linear():
         ws = scale_bytes(rng, (N, K // 32), -10, -4)
         ws_f32 = np.ldexp(np.ones(ws.shape, dtype=np.float32), ws.astype(np.int32) - 127).astype(np.float32)
         out[K] = (x, w, ws, ws_f32)
+    return out
+
+
+DOWN_PROJ_N = 5120
+DOWN_PROJ_K = 2304
+DOWN_PROJ_TP = (1, 2, 4, 8)
+
+
+def down_proj_shards():
+    """{TP: (x [8, K] BF16 bits, W [5120, K] codes, Ws [5120, K/32] bytes)} with
+    K = 2304 / TP: rank 0's share of the shared expert's row-parallel down_proj, seed 5."""
+    rng = np.random.default_rng(5)
+    x = activations(rng, 8, DOWN_PROJ_K)
+    w = weight_codes(rng, (DOWN_PROJ_N, DOWN_PROJ_K))
+    ws = scale_bytes(rng, (DOWN_PROJ_N, DOWN_PROJ_K // 32), -10, -4)
+    out = {}
+    for tp in DOWN_PROJ_TP:
+        K = DOWN_PROJ_K // tp
+        out[tp] = (np.ascontiguousarray(x[:, :K]), np.ascontiguousarray(w[:, :K]),
+                   np.ascontiguousarray(ws[:, : K // 32]))
     return out
 
 
