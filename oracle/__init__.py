@@ -22,9 +22,11 @@ Sources (cited by page title and section):
 * vLLM pull request 56560, "[ROCm][DSv4.1][Perf] Dequantize the MXFP8 weight
   once when dot_scaled cannot be used" (Purpose; Why it is worth a patch;
   review thread) -- MXFP8 dequant, the K % 128 dispatch.
+* The first page again (Implementation) -- checkpoint scale ingestion:
+  group-128 and 128 x 128 scale layouts, FP32 power-of-two scales.
 
 Parity status of each function is listed in its docstring.  Functions with no
 pin independent of themselves say "parity unpinned".
 """
 
-from . import formats, rope, quant, gemm  # noqa: F401
+from . import formats, rope, quant, gemm, ingest  # noqa: F401
