@@ -66,6 +66,9 @@ typedef enum { MX_ROPE_INTERLEAVED = 0, MX_ROPE_NEOX = 1 } mx_rope_style;
 /* Quantisation group of the wo_a activations and weight ([WOA], Summary). */
 #define MX_WOA_GROUP 128
 
+/* Element type of checkpoint scales given to mx_woa_expand_scales. */
+typedef enum { MX_SCALE_E8M0 = 0, MX_SCALE_F32 = 1 } mx_scale_kind;
+
 /* ------------------------------------------------------------------ status */
 
 /* Static text for a status code. */
@@ -87,9 +90,9 @@ void mx_set_dry_run(int on);
 /* Launch counters, in this order: quant, bmm (large tiles), bmm (small T),
  * dequant, linear BF16 branch (prepared weight), linear FP8 branch, linear
  * per-call-dequant branch, f32->e8m0 device, e4m3 encode device, inverse RoPE
- * to BF16, BF16 bmm (large tiles), BF16 bmm (small T).  `out` gets
- * min(n, MX_NUM_COUNTERS) values; returns MX_NUM_COUNTERS. */
-#define MX_NUM_COUNTERS 12
+ * to BF16, BF16 bmm (large tiles), BF16 bmm (small T), wo_a scale expansion.
+ * `out` gets min(n, MX_NUM_COUNTERS) values; returns MX_NUM_COUNTERS. */
+#define MX_NUM_COUNTERS 13
 int mx_get_counters(uint64_t* out, int n);
 void mx_reset_counters(void);
 
@@ -145,6 +148,27 @@ mx_status mx_inv_rope_group_quant(const void* x, const int64_t* positions,
 mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t a_fmt,
                               const uint8_t* w, const uint8_t* w_scale, void* out,
                               int64_t T, int32_t G, int32_t N, int32_t K, void* stream);
+
+/*
+ * mx_woa_expand_scales -- checkpoint weight scales of wo_a -> the layout the
+ * GEMM reads, at load time ([WOA], Implementation: the group-128 weight and
+ * scale layouts are validated before the fast path is used; power-of-two FP32
+ * scales become E8M0 bytes without loss).
+ *
+ * out[g,n,kb] = E8M0 of scale[g, n / block_n, kb].
+ * scale        device [G, ceil(N/block_n), K/128] of E8M0 bytes (MX_SCALE_E8M0) or
+ *              FP32 (MX_SCALE_F32): block_n = 1 is one scale per (g, n, 128-K
+ *              block), block_n = 128 one per 128 x 128 (n, k) block.
+ * out          device u8 [G, N, K/128], the w_scale of mx_bmm_a8w8_mxscale.
+ * reject_count device int32, caller-zeroed, or NULL: FP32 scales that are not
+ *              2^n with -127 <= n <= 127 give 0xFF (NaN) bytes and are counted,
+ *              once per source scale.  A nonzero count means the checkpoint
+ *              cannot take the FP8 path (the caller falls back).  Asynchronous.
+ * Requires: G, N >= 1, K % 128 == 0, G*N*K/128 < 2^31, FP32 scales 4-byte aligned.
+ */
+mx_status mx_woa_expand_scales(const void* scale, int32_t scale_kind, int32_t block_n,
+                               int32_t G, int32_t N, int32_t K, uint8_t* out,
+                               int32_t* reject_count, void* stream);
 
 /* ------------------------------------------------ BF16 arm of wo_a */
 

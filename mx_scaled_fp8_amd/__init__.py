@@ -23,7 +23,7 @@ __all__ = [
     "mx_probe", "mx_version", "mx_set_dry_run", "mx_get_counters", "mx_reset_counters",
     "mx_inv_rope_group_quant", "mx_bmm_a8w8_mxscale", "mx_dequant_mxfp8_to_bf16",
     "mx_linear_dequant_at_load", "mx_linear_workspace_bytes", "mx_linear",
-    "mx_inv_rope_bf16", "mx_bmm_bf16",
+    "mx_inv_rope_bf16", "mx_bmm_bf16", "mx_woa_expand_scales", "MX_SCALE_E8M0", "MX_SCALE_F32",
     "mx_f32_pow2_to_e8m0", "mx_f32_pow2_to_e8m0_device", "mx_f32_to_e4m3_ocp",
     "mx_f32_to_e4m3_fnuz", "mx_f32_to_e4m3_device", "mx_e4m3_to_f32", "mx_e8m0_to_f32",
     "COUNTER_NAMES",
@@ -32,11 +32,12 @@ __all__ = [
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_NOT_LOSSLESS, MX_ERR_HIP = range(5)
 MX_FP8_E4M3_OCP, MX_FP8_E4M3_FNUZ = 0, 1
 MX_ROPE_INTERLEAVED, MX_ROPE_NEOX = 0, 1
+MX_SCALE_E8M0, MX_SCALE_F32 = 0, 1
 MX_LINEAR_K_ALIGN = 128
 MX_LINEAR_BLOCK = 32
 COUNTER_NAMES = ("quant", "bmm_large", "bmm_small", "dequant", "linear_bf16", "linear_fp8",
                  "linear_percall_dequant", "f32_to_e8m0_device", "f32_to_e4m3_device", "rope_bf16",
-                 "bmm_bf16_large", "bmm_bf16_small")
+                 "bmm_bf16_large", "bmm_bf16_small", "expand_scales")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
@@ -74,6 +75,7 @@ def lib():
             "mx_dequant_mxfp8_to_bf16": (ctypes.c_int, [P, P, P, I64, I64, I32, P]),
             "mx_inv_rope_bf16": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, I32, P, P]),
             "mx_bmm_bf16": (ctypes.c_int, [P, P, P, I64, I32, I32, I32, P]),
+            "mx_woa_expand_scales": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P]),
             "mx_linear_dequant_at_load": (ctypes.c_int, [I64]),
             "mx_linear_workspace_bytes": (SZ, [I64, I64, I64, I32]),
             "mx_linear": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P, SZ, P]),
@@ -174,6 +176,20 @@ def mx_bmm_a8w8_mxscale(a, a_scale, w, w_scale, a_fmt=MX_FP8_E4M3_OCP, out=None)
     _check(lib().mx_bmm_a8w8_mxscale(_dev(a, "a", 1), _dev(a_scale, "a_scale", 1), a_fmt, _dev(w, "w", 1),
                                      _dev(w_scale, "w_scale", 1), _dev(out, "out", 2), T, G, N, K, _stream(a)))
     return out
+
+
+def mx_woa_expand_scales(scale, G, N, K, block_n=1, out=None):
+    """Checkpoint scales [G, ceil(N/block_n), K/128] (uint8 E8M0 or float32) ->
+    (uint8 [G, N, K/128], number of rejected FP32 scales)."""
+    kind = MX_SCALE_F32 if scale.dtype == torch.float32 else MX_SCALE_E8M0
+    if kind == MX_SCALE_E8M0 and scale.element_size() != 1:
+        raise ValueError("scale must be uint8 (E8M0) or float32")
+    if out is None:
+        out = torch.empty((G, N, K // 128), dtype=torch.uint8, device=scale.device)
+    rejects = torch.zeros(1, dtype=torch.int32, device=scale.device)
+    _check(lib().mx_woa_expand_scales(_dev(scale, "scale"), kind, block_n, G, N, K, _dev(out, "out", 1),
+                                      _dev(rejects, "reject_count", 4), _stream(scale)))
+    return out, int(rejects.item())
 
 
 # ------------------------------------------------------- BF16 arm of wo_a

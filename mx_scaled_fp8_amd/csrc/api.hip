@@ -31,6 +31,8 @@ mx_status launch_rope_bf16(const void* x, const int64_t* positions, const void* 
                            void* out, hipStream_t stream);
 mx_status launch_bmm_bf16(const void* x, const void* w, void* out, int64_t T, int32_t G, int32_t N, int32_t K,
                           hipStream_t stream);
+mx_status launch_expand_scales(const void* in, int32_t kind, int32_t block_n, int32_t G, int32_t N, int32_t K,
+                               uint8_t* out, int32_t* reject_count, hipStream_t stream);
 
 namespace {
 
@@ -341,6 +343,25 @@ mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const ui
     st = launch_dequant(static_cast<const uint8_t*>(w), w_scale, wb, N, K, MX_LINEAR_BLOCK, s);
     if (st == MX_OK) st = launch_gemm_bf16(x, wb, out, M, N, K, s);
   }
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_woa_expand_scales(const void* scale, int32_t scale_kind, int32_t block_n, int32_t G, int32_t N,
+                               int32_t K, uint8_t* out, int32_t* reject_count, void* stream) {
+  const char* fn = "mx_woa_expand_scales";
+  MX_CHECK(scale_kind == MX_SCALE_E8M0 || scale_kind == MX_SCALE_F32, "%s: unknown scale kind %d", fn, scale_kind);
+  MX_CHECK(block_n == 1 || block_n == 128, "%s: block_n = %d (1 or 128)", fn, block_n);
+  MX_CHECK(G >= 1 && N >= 1 && K >= 128, "%s: G = %d, N = %d, K = %d", fn, G, N, K);
+  MX_CHECK(K % MX_WOA_GROUP == 0, "%s: K = %d is not a multiple of 128 (group-128 layout required)", fn, K);
+  MX_CHECK(static_cast<int64_t>(G) * N * (K / 128) < (int64_t(1) << 31), "%s: G*N*K/128 too large", fn);
+  MX_CHECK(scale && out, "%s: null pointer", fn);
+  MX_CHECK(scale_kind == MX_SCALE_E8M0 || aligned(scale, 4), "%s: FP32 scales must be 4-byte aligned", fn);
+  MX_CHECK(!reject_count || aligned(reject_count, 4), "%s: reject_count must be 4-byte aligned", fn);
+  MX_PREAMBLE();
+  count(C_EXPAND_SCALES);
+  const mx_status st = launch_expand_scales(scale, scale_kind, block_n, G, N, K, out, reject_count,
+                                            static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();
   return st;
 }

@@ -37,6 +37,7 @@ enum Counter {
   C_ROPE_BF16,
   C_BMM_BF16_LARGE,
   C_BMM_BF16_SMALL,
+  C_EXPAND_SCALES,
 };
 void count(Counter c);
 

@@ -70,6 +70,37 @@ __global__ __launch_bounds__(kThreads) void f32_to_e8m0_kernel(const float* __re
   }
 }
 
+// Checkpoint weight scales -> the [G, N, K/128] E8M0 layout the wo_a GEMM
+// reads.  Output byte i = (g, n, kb) takes source (g, n / block_n, kb) of a
+// [G, ceil(N/block_n), K/128] tensor: E8M0 bytes are copied, FP32 scales go
+// through the lossless power-of-two rule above (0xFF where rejected).  A
+// rejected source scale is counted once, by the thread of its block's first row.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void expand_scales_kernel(const void* __restrict__ in, uint8_t* __restrict__ out,
+                                                                 uint32_t total, uint32_t N, uint32_t KB,
+                                                                 uint32_t block_n, int32_t* reject_count) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= total) return;
+  const uint32_t row = i / KB;                   // g * N + n
+  const uint32_t kb = i - row * KB;
+  const uint32_t g = row / N;
+  const uint32_t n = row - g * N;
+  const uint32_t nb = (N + block_n - 1) / block_n;
+  const uint32_t src = (g * nb + n / block_n) * KB + kb;
+  if constexpr (!F32) {
+    out[i] = static_cast<const uint8_t*>(in)[src];
+  } else {
+    const uint32_t u = __float_as_uint(static_cast<const float*>(in)[src]);
+    const uint32_t ef = (u >> 23) & 0xFFu;
+    int b;
+    if (u == 0x00400000u) b = 0;
+    else if ((u >> 31) != 0 || (u & 0x7FFFFFu) != 0 || ef == 0 || ef == 0xFFu) b = -1;
+    else b = static_cast<int>(ef);
+    out[i] = b < 0 ? uint8_t(0xFF) : static_cast<uint8_t>(b);
+    if (b < 0 && reject_count && n % block_n == 0) atomicAdd(reject_count, 1);
+  }
+}
+
 // FP32 -> e4m3, nearest even, saturating.  The FNUZ code of v is the OCP
 // code of 2v (the FNUZ grid is the OCP grid halved, 224 = 448 / 2) with -0
 // mapped to 0x00.
@@ -119,6 +150,21 @@ mx_status launch_f32_to_e4m3(const float* in, uint8_t* out, int64_t n, int32_t f
   else
     f32_to_e4m3_kernel<MX_FP8_E4M3_FNUZ><<<static_cast<uint32_t>(blocks), kThreads, 0, stream>>>(in, out, n);
   return launch_status("mx_f32_to_e4m3_device");
+}
+
+mx_status launch_expand_scales(const void* in, int32_t kind, int32_t block_n, int32_t G, int32_t N, int32_t K,
+                               uint8_t* out, int32_t* reject_count, hipStream_t stream) {
+  const uint32_t KB = static_cast<uint32_t>(K / 128);
+  const uint32_t total = static_cast<uint32_t>(G) * static_cast<uint32_t>(N) * KB;
+  if (total == 0) return MX_OK;
+  const uint32_t blocks = (total + kThreads - 1) / kThreads;
+  if (kind == MX_SCALE_F32)
+    expand_scales_kernel<true><<<blocks, kThreads, 0, stream>>>(in, out, total, static_cast<uint32_t>(N), KB,
+                                                                static_cast<uint32_t>(block_n), reject_count);
+  else
+    expand_scales_kernel<false><<<blocks, kThreads, 0, stream>>>(in, out, total, static_cast<uint32_t>(N), KB,
+                                                                 static_cast<uint32_t>(block_n), reject_count);
+  return launch_status("mx_woa_expand_scales");
 }
 
 }  // namespace mx

@@ -226,6 +226,18 @@ def test_bmm_bf16_validation(dry):
         assert _bmm_bf16(**bad) == mx.MX_ERR_INVALID_ARG, bad
 
 
+def test_expand_scales_validation(dry):
+    f = lambda **kw: _call("mx_woa_expand_scales", kw.get("s", FAKE), kw.get("kind", 1), kw.get("bn", 128),
+                           kw.get("G", 16), kw.get("N", 1024), kw.get("K", 4096), kw.get("o", FAKE),
+                           kw.get("rc", FAKE), None)
+    assert f() == mx.MX_OK
+    assert f(kind=0, bn=1, rc=None) == mx.MX_OK
+    for bad in (dict(kind=2), dict(bn=64), dict(G=0), dict(N=0), dict(K=4000), dict(K=64), dict(s=None),
+                dict(o=None), dict(s=FAKE + 2), dict(rc=FAKE + 1), dict(G=65536, N=65536)):
+        assert f(**bad) == mx.MX_ERR_INVALID_ARG, bad
+    assert f(kind=0, s=FAKE + 1) == mx.MX_OK                           # E8M0 bytes need no alignment
+
+
 def test_converter_validation(dry):
     assert _call("mx_f32_to_e4m3_device", FAKE, FAKE, 10, 0, None) == mx.MX_OK
     assert _call("mx_f32_to_e4m3_device", FAKE, FAKE, 10, 5, None) == mx.MX_ERR_INVALID_ARG
