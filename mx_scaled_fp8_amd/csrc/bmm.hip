@@ -934,10 +934,159 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
   }
 }
 
+// ------------------------------------------ decode batch: T <= 64, K % 1024 == 0
+//
+// One workgroup per (g, 64 n) with all T rows, as bmm_small_kernel, but the
+// operands go global -> LDS by LDS-DMA through a ring of kDecR stages (one
+// 128-byte K-step of the 64 W rows and the 64 A rows each, 16 KiB), so that
+// kDecR - 1 K-steps (112 KiB) per compute unit are in flight and every DMA
+// instruction reads 8 whole 128-byte lines.  The four waves split n (wave w
+// owns rows 16w..16w+15 of the workgroup's W), so every wave consumes every
+// stage and no partial sums are reduced; one barrier per stage recycles the
+// ring.  Each slot is its own __shared__ array and the stage loop is unrolled
+// over the ring, so every access names its slot statically (the compiler can
+// then see that the DMA into one slot does not alias the reads of another).
+constexpr int kDecR = 8;
+constexpr int kDecRows = 64;
+constexpr int kDecStage = 2 * kDecRows * kBK;      // 16 KiB: W rows, then A rows
+constexpr int kDecScaleMax = 16 * 1024;            // staged scale rows: 128 rows x K/128 bytes
+
+template <int KB, bool A_FNUZ>
+__global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s4[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s5[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s6[kDecStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s7[kDecStage];
+  __shared__ __attribute__((aligned(16))) uint8_t scl[kDecScaleMax];   // [64 W rows | 64 A rows][KB]
+  uint8_t* const ring[kDecR] = {s0, s1, s2, s3, s4, s5, s6, s7};
+
+  const int g = blockIdx.x / p.n_groups;
+  const int n0 = (blockIdx.x % p.n_groups) * kDecRows;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const size_t rowA = static_cast<size_t>(p.G) * p.K;
+  static_assert(KB % kDecR == 0 && 2 * kDecRows * KB <= kDecScaleMax, "K-steps");
+
+  // ---- scale rows -> LDS by LDS-DMA as well (an LDS store after the operand
+  // DMA would have to wait for all of it): 128 rows (64 W, 64 A) x KB bytes,
+  // 4 bytes per lane, 256 bytes per instruction, KB/8 instructions per wave;
+  // issued before the operand stages, so the first stage's wait covers them
+  constexpr int kScInstr = KB / 8;
+#pragma unroll
+  for (int it = 0; it < kScInstr; ++it) {
+    const int ii = wave * kScInstr + it;
+    const int byte = ii * 256 + 4 * lane;
+    const int r = byte / KB, off = byte - r * KB;
+    const uint8_t* src = r < kDecRows
+        ? p.sw + (static_cast<size_t>(g) * p.N + min(n0 + r, p.N - 1)) * KB + off
+        : p.sa + (static_cast<size_t>(min(r - kDecRows, p.T - 1)) * p.G + g) * KB + off;
+    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(scl + ii * 256), 4, 0, 0);
+  }
+
+  // ---- DMA: wave w fills W rows 16w..16w+15 and A rows 16w..16w+15 of a stage,
+  // 8 rows per instruction (lane i writes LDS byte 16i of the instruction's
+  // 1 KiB); the global side reads the chunk that the swizzle puts at lane i
+  const uint8_t* pW[2];
+  const uint8_t* pA[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int r = 16 * wave + 8 * it + (lane >> 3);
+    const uint32_t chunk = static_cast<uint32_t>((lane & 7) ^ swz8(r)) * 16;
+    pW[it] = p.w + (static_cast<size_t>(g) * p.N + min(n0 + r, p.N - 1)) * p.K + chunk;
+    pA[it] = p.a + static_cast<size_t>(min(r, p.T - 1)) * rowA + static_cast<size_t>(g) * p.K + chunk;
+  }
+  auto issue = [&](uint8_t* slot, int kt) {
+    const size_t ko = static_cast<size_t>(min(kt, KB - 1)) * kBK;   // past the end: a harmless refetch
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int rb = 16 * wave + 8 * it;
+      __builtin_amdgcn_global_load_lds(pW[it] + ko, (lds_void_t*)(slot + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pA[it] + ko, (lds_void_t*)(slot + (kDecRows + rb) * kBK), 16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kDecR - 1; ++u) issue(ring[u], u);
+
+  // ---- fragments: lane l holds row l%16 of a 16-row tile; K bytes 16q.. and
+  // 64+16q.. (q = l/16) sit at physical chunks q ^ s and (q + 4) ^ s
+  const int sw16 = swz8(lane & 15);
+  const int q = lane >> 4;
+  const int c0 = (q ^ sw16) * 16, c1 = ((q + 4) ^ sw16) * 16;
+  const int rdW = (16 * wave + (lane & 15)) * kBK;
+  const uint8_t* sclW = scl + (16 * wave + (lane & 15)) * KB;
+  const uint8_t* sclA = scl + (kDecRows + (lane & 15)) * KB;
+  v4f acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int kWaitStage = 0x4078;                 // vmcnt(24) lgkmcnt(0): 4 instructions x (kDecR - 2) stages
+  static_assert(4 * (kDecR - 2) == 24, "wait count");
+
+#pragma unroll 1
+  for (int kt0 = 0; kt0 < KB; kt0 += kDecR) {
+#pragma unroll
+    for (int u = 0; u < kDecR; ++u) {
+      const int kt = kt0 + u;
+      __builtin_amdgcn_s_waitcnt(kWaitStage);       // this wave's part of stage kt is in LDS
+      __builtin_amdgcn_s_barrier();                 // everyone's part; everyone is done with stage kt-1
+      issue(ring[(u + kDecR - 1) % kDecR], kt + kDecR - 1);
+      const uint8_t* st = ring[u];
+      // all of the stage's reads, then its MFMAs
+      const v8i fw = make_v8i(*reinterpret_cast<const uint4*>(st + rdW + c0),
+                              *reinterpret_cast<const uint4*>(st + rdW + c1));
+      v8i fa[4];
+      int sa_[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint8_t* ra = st + (kDecRows + 16 * j + (lane & 15)) * kBK;
+        fa[j] = make_v8i(*reinterpret_cast<const uint4*>(ra + c0), *reinterpret_cast<const uint4*>(ra + c1));
+        sa_[j] = sclA[16 * j * KB + kt];
+        if (A_FNUZ) sa_[j] = fnuz_scale_to_ocp(sa_[j]);   // FNUZ activation scale -> OCP scale
+      }
+      const int sw_ = sclW[kt];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_scaled(fw, fa[j], acc[j], sw_, sa_[j]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
+
+  // ---- C layout: lane l holds column l%16 (a token) and rows 4(l/16)..+3 (n)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = 16 * j + (lane & 15);
+    const int n = n0 + 16 * wave + 4 * q;
+    if (t < p.T && n < p.N)
+      *reinterpret_cast<uint2*>(p.out + (static_cast<size_t>(t) * p.G + g) * p.N + n) = pack4_bf16(acc[j]);
+  }
+}
+
 // LDS the small-T kernel stages its scale rows in (dynamic shared memory).
 constexpr size_t kSmallScaleLdsMax = 48 * 1024;
 template <int NT, int SB>
 constexpr size_t small_scale_lds(int K) { return static_cast<size_t>(16 * NT + 64) * (K / SB); }
+
+template <int KB>
+void launch_decode_kb(const SmallArgs& a, bool fnuz, hipStream_t s) {
+  const int grid = a.G * a.n_groups;
+  if (fnuz)
+    bmm_decode_kernel<KB, true><<<grid, 256, 0, s>>>(a);
+  else
+    bmm_decode_kernel<KB, false><<<grid, 256, 0, s>>>(a);
+}
+
+// K = 1024, 2048, 4096 or 8192
+void launch_decode(const SmallArgs& a, bool fnuz, hipStream_t s) {
+  switch (a.K / kBK) {
+    case 8: launch_decode_kb<8>(a, fnuz, s); break;
+    case 16: launch_decode_kb<16>(a, fnuz, s); break;
+    case 32: launch_decode_kb<32>(a, fnuz, s); break;
+    default: launch_decode_kb<64>(a, fnuz, s); break;
+  }
+}
 
 template <int NT, int SB>
 void launch_small(const SmallArgs& a, bool fnuz, hipStream_t s) {
@@ -956,6 +1105,12 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
                      void* out, int64_t T, int32_t G, int32_t N, int32_t K, hipStream_t stream) {
   if (T == 0) return MX_OK;
   const bool fnuz = a_fmt == MX_FP8_E4M3_FNUZ;
+  if (T <= 64 && (K == 1024 || K == 2048 || K == 4096 || K == 8192) && aligned(sa, 4) && aligned(sw, 4)) {
+    SmallArgs s{a, sa, w, sw, static_cast<uint16_t*>(out), static_cast<int>(T), G, N, K, (N + kDecRows - 1) / kDecRows};
+    launch_decode(s, fnuz, stream);
+    count(C_BMM_SMALL);
+    return launch_status("mx_bmm_a8w8_mxscale (decode batch)");
+  }
   if (T <= 64 && small_scale_lds<4, 128>(K) <= kSmallScaleLdsMax) {   // (else the tiled kernels)
     SmallArgs s{a, sa, w, sw, static_cast<uint16_t*>(out), static_cast<int>(T), G, N, K, (N + 63) / 64};
     launch_small<4, 128>(s, fnuz, stream);

@@ -58,6 +58,33 @@ def test_random_operands(T, Gn, N, K):
     assert_gemm_close(out, ref, f"T={T} G={Gn} N={N} K={K}")
 
 
+# T <= 64 with K in {1024, 2048, 4096, 8192} takes the decode-batch kernel
+# (LDS-DMA ring of 8 K-steps): a single token, a ragged last n-block, the
+# deepest and the shallowest K, and FNUZ activations
+DECODE_SHAPES = [(1, 1, 16, 1024), (5, 3, 112, 2048), (64, 2, 272, 8192), (33, 16, 1024, 4096), (64, 1, 64, 1024)]
+
+
+@pytest.mark.parametrize("T,Gn,N,K", DECODE_SHAPES)
+def test_decode_kernel(T, Gn, N, K):
+    a, sa, w, sw = workloads.gemm_operands(5000 + T + N + K, T, Gn, N, K)
+    say("bmm decode kernel", T, Gn, N, K)
+    out = _gpu_bmm(a, sa, w, sw)
+    assert_gemm_close(out, G.bmm_a8w8_mxscale(a, sa, w, sw), f"T={T} G={Gn} N={N} K={K}")
+
+
+def test_decode_kernel_fnuz():
+    T, Gn, N, K = 64, 2, 192, 2048
+    a, sa, w, sw = workloads.gemm_operands(77, T, Gn, N, K, a_exp=(-12, -2))
+    # the same values in FNUZ: code unchanged, scale + 1, -0 -> 0
+    fz = np.where(a == 0x80, 0, a).astype(np.uint8)
+    sz = (sa.astype(int) + 1).astype(np.uint8)
+    say("bmm decode kernel fnuz")
+    out_f = _gpu_bmm(fz, sz, w, sw, mx.MX_FP8_E4M3_FNUZ)
+    out_o = _gpu_bmm(a, sa, w, sw)
+    assert np.array_equal(out_f, out_o)
+    assert_gemm_close(out_f, G.bmm_a8w8_mxscale(fz, sz, w, sw, F.FNUZ), "decode fnuz")
+
+
 # K = 2048 and 4096 (16 or 32 K-stages) take the persistent kernel: tile counts
 # below one per XCD, one per workgroup, and several per workgroup (T = 4200:
 # 340 tiles on 256 workgroups), with ragged T and N tiles.  Large cases are
