@@ -948,10 +948,22 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
 // then see that the DMA into one slot does not alias the reads of another).
 constexpr int kDecR = 8;
 constexpr int kDecRows = 64;
+// operand modes of the decode kernel: FP8 A in OCP or FNUZ bytes (E8M0
+// scales), or BF16 A and W (no scales; a stage is then 64 elements and the
+// K and row strides in SmallArgs are in bytes)
+constexpr int kDecOcp = 0, kDecFnuz = 1, kDecBf16 = 2;
+
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+template <int H>
+__device__ __forceinline__ v8bf_t bf16_half(const v8i& v) {
+  const v4i_t h = __builtin_shufflevector(v, v, 4 * H, 4 * H + 1, 4 * H + 2, 4 * H + 3);
+  return __builtin_bit_cast(v8bf_t, h);
+}
 constexpr int kDecStage = 2 * kDecRows * kBK;      // 16 KiB: W rows, then A rows
 constexpr int kDecScaleMax = 16 * 1024;            // staged scale rows: 128 rows x K/128 bytes
 
-template <int KB, bool A_FNUZ>
+template <int KB, int MODE>
 __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s0[kDecStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[kDecStage];
@@ -976,7 +988,7 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   // DMA would have to wait for all of it): 128 rows (64 W, 64 A) x KB bytes,
   // 4 bytes per lane, 256 bytes per instruction, KB/8 instructions per wave;
   // issued before the operand stages, so the first stage's wait covers them
-  constexpr int kScInstr = KB / 8;
+  constexpr int kScInstr = MODE == kDecBf16 ? 0 : KB / 8;
 #pragma unroll
   for (int it = 0; it < kScInstr; ++it) {
     const int ii = wave * kScInstr + it;
@@ -1039,17 +1051,29 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
       const v8i fw = make_v8i(*reinterpret_cast<const uint4*>(st + rdW + c0),
                               *reinterpret_cast<const uint4*>(st + rdW + c1));
       v8i fa[4];
-      int sa_[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint8_t* ra = st + (kDecRows + 16 * j + (lane & 15)) * kBK;
         fa[j] = make_v8i(*reinterpret_cast<const uint4*>(ra + c0), *reinterpret_cast<const uint4*>(ra + c1));
-        sa_[j] = sclA[16 * j * KB + kt];
-        if (A_FNUZ) sa_[j] = fnuz_scale_to_ocp(sa_[j]);   // FNUZ activation scale -> OCP scale
       }
-      const int sw_ = sclW[kt];
+      if constexpr (MODE == kDecBf16) {
+        // a lane's two 16-byte chunks are its K-pieces of two 16x16x32 BF16 MFMAs
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = mfma_scaled(fw, fa[j], acc[j], sw_, sa_[j]);
+        for (int j = 0; j < 4; ++j) {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16_half<0>(fw), bf16_half<0>(fa[j]), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bf16_half<1>(fw), bf16_half<1>(fa[j]), acc[j], 0, 0, 0);
+        }
+      } else {
+        int sa_[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sa_[j] = sclA[16 * j * KB + kt];
+          if (MODE == kDecFnuz) sa_[j] = fnuz_scale_to_ocp(sa_[j]);   // FNUZ activation scale -> OCP scale
+        }
+        const int sw_ = sclW[kt];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = mfma_scaled(fw, fa[j], acc[j], sw_, sa_[j]);
+      }
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
@@ -1069,22 +1093,14 @@ constexpr size_t kSmallScaleLdsMax = 48 * 1024;
 template <int NT, int SB>
 constexpr size_t small_scale_lds(int K) { return static_cast<size_t>(16 * NT + 64) * (K / SB); }
 
-template <int KB>
-void launch_decode_kb(const SmallArgs& a, bool fnuz, hipStream_t s) {
+template <int MODE>
+void launch_decode(const SmallArgs& a, hipStream_t s) {   // a.K (bytes) = 1024, 2048, 4096 or 8192
   const int grid = a.G * a.n_groups;
-  if (fnuz)
-    bmm_decode_kernel<KB, true><<<grid, 256, 0, s>>>(a);
-  else
-    bmm_decode_kernel<KB, false><<<grid, 256, 0, s>>>(a);
-}
-
-// K = 1024, 2048, 4096 or 8192
-void launch_decode(const SmallArgs& a, bool fnuz, hipStream_t s) {
   switch (a.K / kBK) {
-    case 8: launch_decode_kb<8>(a, fnuz, s); break;
-    case 16: launch_decode_kb<16>(a, fnuz, s); break;
-    case 32: launch_decode_kb<32>(a, fnuz, s); break;
-    default: launch_decode_kb<64>(a, fnuz, s); break;
+    case 8: bmm_decode_kernel<8, MODE><<<grid, 256, 0, s>>>(a); break;
+    case 16: bmm_decode_kernel<16, MODE><<<grid, 256, 0, s>>>(a); break;
+    case 32: bmm_decode_kernel<32, MODE><<<grid, 256, 0, s>>>(a); break;
+    default: bmm_decode_kernel<64, MODE><<<grid, 256, 0, s>>>(a); break;
   }
 }
 
@@ -1107,7 +1123,10 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
   const bool fnuz = a_fmt == MX_FP8_E4M3_FNUZ;
   if (T <= 64 && (K == 1024 || K == 2048 || K == 4096 || K == 8192) && aligned(sa, 4) && aligned(sw, 4)) {
     SmallArgs s{a, sa, w, sw, static_cast<uint16_t*>(out), static_cast<int>(T), G, N, K, (N + kDecRows - 1) / kDecRows};
-    launch_decode(s, fnuz, stream);
+    if (fnuz)
+      launch_decode<kDecFnuz>(s, stream);
+    else
+      launch_decode<kDecOcp>(s, stream);
     count(C_BMM_SMALL);
     return launch_status("mx_bmm_a8w8_mxscale (decode batch)");
   }
@@ -1160,6 +1179,19 @@ mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* 
               static_cast<int>(K), static_cast<int>((N + 15) / 16)};
   launch_small<1, 32>(s, false, stream);
   return launch_status("mx_linear (block-scaled FP8 GEMM)");
+}
+
+// BF16 decode batch of the BF16 wo_a arm on the decode kernel: x [T, G, K],
+// W [G, N, K] BF16, T <= 64, K in {512, 1024, 2048, 4096} (a row of 1, 2, 4 or
+// 8 KiB); false if the shape is not one of these.
+bool launch_bmm_bf16_decode(const void* x, const void* w, void* out, int64_t T, int32_t G, int32_t N, int32_t K,
+                            hipStream_t stream) {
+  const int bytes = 2 * K;
+  if (T > 64 || !(bytes == 1024 || bytes == 2048 || bytes == 4096 || bytes == 8192)) return false;
+  SmallArgs a{static_cast<const uint8_t*>(x), nullptr, static_cast<const uint8_t*>(w), nullptr,
+              static_cast<uint16_t*>(out), static_cast<int>(T), G, N, bytes, (N + kDecRows - 1) / kDecRows};
+  launch_decode<kDecBf16>(a, stream);
+  return true;
 }
 
 }  // namespace mx

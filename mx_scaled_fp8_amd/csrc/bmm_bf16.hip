@@ -21,8 +21,9 @@
 // passes against 32 of 16), so the pipeline keeps its timing and moves twice
 // the bytes per flop.
 //
-// T <= 64 (decode): the split-K BF16 kernel of the MXFP8 linear, one launch
-// over all groups.
+// T <= 64 (decode): the FP8 decode-batch kernel's LDS-DMA ring with BF16
+// MFMAs for K of 512 to 4096, else the split-K BF16 kernel of the MXFP8
+// linear, one launch over all groups.
 #include <algorithm>
 #include <type_traits>
 
@@ -32,6 +33,8 @@ namespace mx {
 
 mx_status launch_gemm_bf16_strided(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K,
                                    int32_t G, int64_t ldx, int64_t ldo, hipStream_t stream);
+bool launch_bmm_bf16_decode(const void* x, const void* w, void* out, int64_t T, int32_t G, int32_t N, int32_t K,
+                            hipStream_t stream);
 
 namespace {
 
@@ -312,6 +315,10 @@ mx_status launch_bmm_bf16(const void* x, const void* w, void* out, int64_t T, in
                           hipStream_t stream) {
   if (T == 0) return MX_OK;
   const int cus = device_cu_count();
+  if (T <= 64 && launch_bmm_bf16_decode(x, w, out, T, G, N, K, stream)) {
+    count(C_BMM_BF16_SMALL);
+    return launch_status("mx_bmm_bf16 (decode batch)");
+  }
   if (T <= 64 || cus < 8) {
     count(C_BMM_BF16_SMALL);
     return launch_gemm_bf16_strided(x, w, out, T, N, K, G, static_cast<int64_t>(G) * K,

@@ -6,7 +6,8 @@
   outside the table (NaN in the rotated dims only), ragged and production
   head layouts.
 * Batched BF16 GEMM: |gpu - ref| <= 2^-7 |ref| + 1e-3 rms(ref) against the
-  fp64 oracle over the small-T kernel (T <= 64) and the persistent tiles
+  fp64 oracle over both small-T kernels (T <= 64: the LDS-DMA decode kernel
+  for K of 512 to 4096, the split-K kernel otherwise) and the persistent tiles
   (K = 128 is a tile of only the two transition stages; ragged T and N
   tiles; several tiles per workgroup), run-to-run determinism.
 * End to end: rotation, the group-128 dequantised weight, the GEMM, on the
@@ -123,7 +124,8 @@ def _gpu_bmm_bf16(x, w):
 
 
 BMM_SHAPES = [
-    (1, 1, 16, 128), (7, 2, 48, 256), (64, 3, 128, 512), (16, 2, 1024, 4096),        # small T
+    (1, 1, 16, 128), (7, 2, 48, 256),                                                 # small T, split-K kernel
+    (64, 3, 128, 512), (16, 2, 1024, 4096), (33, 2, 272, 2048), (1, 1, 64, 1024),     # small T, decode kernel
     (65, 1, 16, 128), (300, 2, 272, 384), (256, 1, 256, 128), (513, 2, 784, 256),    # persistent
 ]
 
