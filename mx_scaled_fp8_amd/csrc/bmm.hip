@@ -1088,6 +1088,113 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   }
 }
 
+// --------------------------- MXFP8 linear, block-32 scales, M <= 64 (LDS-DMA)
+//
+// The decode kernel's ring for the linear's shapes (N of a few thousand, K a
+// multiple of 128 but not of 1024): one workgroup per 16 columns n, so that
+// N = 4096 still gives 256 workgroups; a stage is one 128-byte K-step of the
+// 16 W rows and the 64 x rows (10 KiB), kLinR of them in the ring; wave w
+// owns token tile w (x rows 16w..16w+15), one MFMA per stage.  A stage is
+// moved by 12 DMA instructions, 3 per wave: the ten that carry its rows and
+// two that re-read x rows 0..15 into 2 KiB of the slot nobody reads.  A DMA
+// issued on some waves only would leave the compiler unsure which LDS it
+// writes, and it would then drain all DMA before the scale reads.
+constexpr int kLinR = 8;                    // (the compiler tracks 9 LDS-DMA targets: 8 slots + scales)
+constexpr int kLinRowsW = 16;
+constexpr int kLinRows = kLinRowsW + 64;
+constexpr int kLinStage = (kLinRows + 16) * kBK;   // 10 KiB of rows + 2 KiB written by the padding DMA
+constexpr int kLinScaleMax = kLinRows * 256;       // scale rows of K <= 8192
+
+__global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s0[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s1[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s3[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s4[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s5[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s6[kLinStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s7[kLinStage];
+  __shared__ __attribute__((aligned(16))) uint8_t scl[kLinScaleMax];   // [16 W rows | 64 x rows][K/32]
+  uint8_t* const ring[kLinR] = {s0, s1, s2, s3, s4, s5, s6, s7};
+
+  const int n0 = blockIdx.x * kLinRowsW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = p.K / kBK;
+  const int SPK = p.K / 32;                           // scale bytes per row (a multiple of 4)
+
+  // ---- scale rows by LDS-DMA, 4 bytes per lane, before the operand stages
+  const int sc_bytes = kLinRows * SPK;
+  for (int ii = wave; ii * 256 < sc_bytes; ii += 4) {
+    const int byte = ii * 256 + 4 * lane;
+    if (byte < sc_bytes) {
+      const int r = byte / SPK, off = byte - r * SPK;
+      const uint8_t* src = r < kLinRowsW ? p.sw + static_cast<size_t>(min(n0 + r, p.N - 1)) * SPK + off
+                                         : p.sa + static_cast<size_t>(min(r - kLinRowsW, p.T - 1)) * SPK + off;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(scl + ii * 256), 4, 0, 0);
+    }
+  }
+
+  // ---- operand DMA: instruction ii (0..11) of a stage moves its rows
+  // 8ii..8ii+7 (W rows 0..15, x rows 0..63, then the padding rows 80..95,
+  // read from x rows 0..15); wave w issues ii = w, w + 4, w + 8
+  const uint8_t* src_row[3];
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int ii = wave + 4 * it;
+    const int r = 8 * ii + (lane >> 3);               // stage row
+    const int xr = r < kLinRows ? r - kLinRowsW : r - kLinRows;   // x row (padding: rows 0..15 again)
+    const uint32_t chunk = static_cast<uint32_t>((lane & 7) ^ swz8(r)) * 16;
+    src_row[it] = r < kLinRowsW ? p.w + static_cast<size_t>(min(n0 + r, p.N - 1)) * p.K + chunk
+                                : p.a + static_cast<size_t>(min(xr, p.T - 1)) * p.K + chunk;
+  }
+  auto issue = [&](uint8_t* slot, int kt) {
+    const size_t ko = static_cast<size_t>(min(kt, KB - 1)) * kBK;   // past the end: a harmless refetch
+#pragma unroll
+    for (int it = 0; it < 3; ++it)
+      __builtin_amdgcn_global_load_lds(src_row[it] + ko, (lds_void_t*)(slot + 8 * (wave + 4 * it) * kBK), 16, 0, 0);
+  };
+#pragma unroll
+  for (int u = 0; u < kLinR - 1; ++u) issue(ring[u], u);
+
+  // ---- fragments (as the decode kernel) and block-32 scales: lane group q's
+  // byte is block 4kt + q of its row
+  const int sw16 = swz8(lane & 15);
+  const int q = lane >> 4;
+  const int c0 = (q ^ sw16) * 16, c1 = ((q + 4) ^ sw16) * 16;
+  const int rdW = (lane & 15) * kBK;
+  const int rdA = (kLinRowsW + 16 * wave + (lane & 15)) * kBK;
+  const uint8_t* sclW = scl + (lane & 15) * SPK + q;
+  const uint8_t* sclA = scl + (kLinRowsW + 16 * wave + (lane & 15)) * SPK + q;
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  constexpr int kWaitStage = 0x4072;                 // vmcnt(18) lgkmcnt(0): 3 instructions x (kLinR - 2) stages
+  static_assert(3 * (kLinR - 2) == 18, "wait count");
+
+#pragma unroll 1
+  for (int kt0 = 0; kt0 < KB; kt0 += kLinR) {
+#pragma unroll
+    for (int u = 0; u < kLinR; ++u) {
+      const int kt = kt0 + u;
+      if (kt >= KB) break;                          // uniform: every wave leaves at the same stage
+      __builtin_amdgcn_s_waitcnt(kWaitStage);
+      __builtin_amdgcn_s_barrier();
+      issue(ring[(u + kLinR - 1) % kLinR], kt + kLinR - 1);
+      const uint8_t* st = ring[u];
+      const v8i fw = make_v8i(*reinterpret_cast<const uint4*>(st + rdW + c0),
+                              *reinterpret_cast<const uint4*>(st + rdW + c1));
+      const v8i fa = make_v8i(*reinterpret_cast<const uint4*>(st + rdA + c0),
+                              *reinterpret_cast<const uint4*>(st + rdA + c1));
+      acc = mfma_scaled(fw, fa, acc, sclW[4 * kt], sclA[4 * kt]);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
+
+  const int t = 16 * wave + (lane & 15);
+  const int n = n0 + 4 * q;
+  if (t < p.T && n < p.N) *reinterpret_cast<uint2*>(p.out + static_cast<size_t>(t) * p.N + n) = pack4_bf16(acc);
+}
+
 // LDS the small-T kernel stages its scale rows in (dynamic shared memory).
 constexpr size_t kSmallScaleLdsMax = 48 * 1024;
 template <int NT, int SB>
@@ -1172,6 +1279,12 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
+  if (K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
+    SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
+                static_cast<int>(K), static_cast<int>((N + kLinRowsW - 1) / kLinRowsW)};
+    gemm_mx32_dma_kernel<<<s.n_groups, 256, 0, stream>>>(s);
+    return launch_status("mx_linear (block-scaled FP8 GEMM)");
+  }
   if (small_scale_lds<1, 32>(static_cast<int>(K)) > kSmallScaleLdsMax)
     return fail(MX_ERR_UNSUPPORTED, "mx_linear: K = %lld is too large for the block-scaled FP8 path (at most %zu)",
                 static_cast<long long>(K), kSmallScaleLdsMax / 80 * 32);
