@@ -1122,7 +1122,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = p.K / kBK;
-  const int SPK = p.K / 32;                           // scale bytes per row (a multiple of 4)
+  const int SPK = 4 * KB;                             // scale bytes per row (block 32)
 
   // ---- scale rows by LDS-DMA, 4 bytes per lane, before the operand stages
   const int sc_bytes = kLinRows * SPK;
@@ -1171,6 +1171,8 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
   constexpr int kWaitStage = 0x4072;                 // vmcnt(18) lgkmcnt(0): 3 instructions x (kLinR - 2) stages
   static_assert(3 * (kLinR - 2) == 18, "wait count");
 
+  // (the compiler drains the DMA once per pass of this loop, at its head:
+  // it cannot tell which slot the DMA pending there writes)
 #pragma unroll 1
   for (int kt0 = 0; kt0 < KB; kt0 += kLinR) {
 #pragma unroll

@@ -110,6 +110,19 @@ def test_aligned_control_k2048():
     assert_gemm_close(out, G.mx_linear(x, w, ws, 32), "K=2048")
 
 
+@pytest.mark.parametrize("K", [1024, 3072, 4096, 8192])
+def test_linear_fp8_other_k(K):
+    """Block-scaled branch at K that take the run-time stage count (and the
+    deepest K the scale rows allow)."""
+    rng = np.random.default_rng(K)
+    x = workloads.activations(rng, 64, K)
+    w = workloads.weight_codes(rng, (272, K))
+    ws = workloads.scale_bytes(rng, (272, K // 32), -10, -4)
+    say("mx_linear fp8", K)
+    out = host_u16(mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws)))
+    assert_gemm_close(out, G.mx_linear(x, w, ws, 32), f"K={K}")
+
+
 @pytest.mark.parametrize("M", [1, 5, 64])
 def test_linear_small_m(M):
     rng = np.random.default_rng(30 + M)
