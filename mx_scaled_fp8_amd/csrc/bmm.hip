@@ -1281,7 +1281,10 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
-  if (K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
+  // the LDS-DMA ring for more than 16 rows (M = 64, N = 4096: 10.9 -> 7.8 us at
+  // K = 1152); up to 16 rows the register-staged kernel below was faster (M = 1,
+  // N = 5120, K = 2304: 13 against 16 us), since the ring moves 64 x rows per stage
+  if (M > 16 && K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
     SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
                 static_cast<int>(K), static_cast<int>((N + kLinRowsW - 1) / kLinRowsW)};
     gemm_mx32_dma_kernel<<<s.n_groups, 256, 0, stream>>>(s);

@@ -93,11 +93,88 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const uint16_t* __restri
   }
 }
 
+// Decode-sized M with a short K (the linear's BF16 branch: K = 288 or 576 at
+// the pages' shapes): a wave has at most MAXS K-steps, so it issues the loads
+// of all of them before its first MFMA and pays one memory latency, not one
+// per step.  MT row tiles of 16, 16 columns n per workgroup.
+template <int MT, int MAXS>
+__global__ __launch_bounds__(256) void gemm_bf16_upfront_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ w,
+                                                                uint16_t* __restrict__ out, int M, int N, int K,
+                                                                int n_groups) {
+  __shared__ float red[4][MT][4][64];
+  const int n0 = (blockIdx.x % n_groups) * 16;
+  const int m0 = blockIdx.y * 16 * MT;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int KS = K / 32;
+  const int kq = (lane >> 4) * 8;           // element offset inside the 32-wide step
+  const uint16_t* pw = w + static_cast<size_t>(min(n0 + (lane & 15), N - 1)) * K + kq;
+  const uint16_t* px[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) px[j] = x + static_cast<size_t>(min(m0 + j * 16 + (lane & 15), M - 1)) * K + kq;
+
+  v8bf fw[MAXS], fx[MAXS][MT];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {          // steps past the end load the last step (never used)
+    const int ko = min(wave + 4 * s, KS - 1) * 32;
+    fw[s] = as_v8bf(*reinterpret_cast<const uint4*>(pw + ko));
+#pragma unroll
+    for (int j = 0; j < MT; ++j) fx[s][j] = as_v8bf(*reinterpret_cast<const uint4*>(px[j] + ko));
+  }
+  v4f acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (wave + 4 * s < KS) {                // uniform per wave
+#pragma unroll
+      for (int j = 0; j < MT; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[s], fx[s][j], acc[j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < MT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][j][r][lane] = acc[j][r];
+  __syncthreads();
+  for (int j = wave; j < MT; j += 4) {
+    float v[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = red[0][j][r][lane] + red[1][j][r][lane] + red[2][j][r][lane] + red[3][j][r][lane];
+    const int m = m0 + j * 16 + (lane & 15);
+    const int n = n0 + (lane >> 4) * 4;
+    if (m < M && n < N)
+      *reinterpret_cast<uint2*>(out + static_cast<size_t>(m) * N + n) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  }
+}
+
+template <int MT, int MAXS>
+void launch_upfront(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int n_groups = static_cast<int>((N + 15) / 16);
+  const dim3 grid(n_groups, static_cast<unsigned>((M + 16 * MT - 1) / (16 * MT)));
+  gemm_bf16_upfront_kernel<MT, MAXS><<<grid, 256, 0, stream>>>(
+      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), static_cast<uint16_t*>(out),
+      static_cast<int>(M), static_cast<int>(N), static_cast<int>(K), n_groups);
+}
+
+template <int MT>
+bool launch_upfront_k(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  const int64_t steps = (K / 32 + 3) / 4;   // K-steps of wave 0
+  if (steps <= 3) launch_upfront<MT, 3>(x, w, out, M, N, K, stream);
+  else if (steps <= 5) launch_upfront<MT, 5>(x, w, out, M, N, K, stream);
+  else if (steps <= 8) launch_upfront<MT, 8>(x, w, out, M, N, K, stream);
+  else return false;
+  return true;
+}
+
 }  // namespace
 
 mx_status launch_gemm_bf16(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K,
                            hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
+  // up to 16 rows (a decode batch): all loads up front (measured 4.5 -> 3.7 us at
+  // N = 5120, K = 576, M = 1); more rows: the split-K loop below was as fast
+  if (M <= 16 && launch_upfront_k<1>(x, w, out, M, N, K, stream)) return launch_status("mx_linear (BF16 GEMM)");
   const int n_groups = static_cast<int>((N + 15) / 16);
   const dim3 grid(n_groups, static_cast<unsigned>((M + 63) / 64));
   gemm_bf16_kernel<1><<<grid, 256, 0, stream>>>(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),

@@ -123,7 +123,7 @@ def test_linear_fp8_other_k(K):
     assert_gemm_close(out, G.mx_linear(x, w, ws, 32), f"K={K}")
 
 
-@pytest.mark.parametrize("M", [1, 5, 64])
+@pytest.mark.parametrize("M", [1, 5, 16, 17, 33, 64])
 def test_linear_small_m(M):
     rng = np.random.default_rng(30 + M)
     for K in (288, 1152):
