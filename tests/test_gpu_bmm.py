@@ -169,14 +169,28 @@ def test_deterministic():
     assert np.array_equal(_gpu_bmm(a, sa, w, sw), _gpu_bmm(a, sa, w, sw))
 
 
-def test_special_scales():
-    """E8M0 0xFF scales make their block NaN; scale byte 0 (2^-127) is honoured."""
-    T, Gn, N, K = 32, 1, 32, 256
+@pytest.mark.parametrize("K", [256, 1024])          # the split-K small kernel and the decode kernel
+def test_special_scales(K):
+    """E8M0 0xFF scales make their block NaN (an activation scale: one token's
+    row; a weight scale: one column); scale byte 0 (2^-127) is honoured."""
+    T, Gn, N = 32, 1, 80
     a, sa, w, sw = workloads.gemm_operands(9, T, Gn, N, K)
     sa[0, 0, 1] = 0xFF
+    sw[0, 5, 0] = 0xFF
+    sa[3, 0, :] = 0                                    # 2^-127 on every block of token 3
     out = F.bf16_to_f64(_gpu_bmm(a, sa, w, sw))
     assert np.all(np.isnan(out[0, 0, :]))
-    assert not np.isnan(out[1:]).any()
+    assert np.all(np.isnan(out[:, 0, 5]))
+    keep = np.ones(out.shape, bool)
+    keep[0] = False
+    keep[:, :, 5] = False
+    assert not np.isnan(out[keep]).any()
+    ref3 = G.bmm_a8w8_mxscale(a[3:4], sa[3:4], w, sw)[0, 0]
+    cols = [n for n in range(N) if n != 5]
+    assert np.all(np.abs(ref3[cols]) < 2.0 ** -100)     # tiny, yet normal in fp32 and BF16
+    assert_gemm_close(_gpu_bmm(a, sa, w, sw)[3:4][:, :, cols], ref3[None, None, cols], "2^-127 scales")
+    ref = G.bmm_a8w8_mxscale(a[1:], sa[1:], w, sw)
+    assert_gemm_close(_gpu_bmm(a, sa, w, sw)[1:][:, :, cols], ref[:, :, cols], f"special scales K={K}")
 
 
 def _sampled_check(p, q_dev, s_dev, rows, what):
