@@ -590,6 +590,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
   constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
   constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
+  constexpr int kWaitOlder32 = 0x8070;           // vmcnt(32) lgkmcnt(0)
 
   // front / back: the two halves of a stage, as in bmm_large_kernel.  back()
   // fetches stage `dma_kb` of the DMA tile into `cur` and reads the scales of
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // front(cur, first, with_scales): `first` starts the tile's sums;
   // `with_scales` also writes the next tile's staged scales (load_scales) to
   // LDS buffer `scale_sb` before the barrier, so they are visible after it.
-  auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb) {
+  auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb, bool stores_pending = false) {
     __builtin_amdgcn_sched_barrier(0);
     mma_half(fw[0], fa[0], swv, sav, first);
     read_half(cur, ch10, ch11, fw[1], fa[1]);
@@ -611,7 +612,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    if (stores_pending)
+      __builtin_amdgcn_s_waitcnt(kWaitOlder32);          // all but the previous tile's 32 output stores
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
     if constexpr (decltype(with_scales)::value) {
       store_scales(scale_sb);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -661,8 +665,9 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
 
   const std::true_type yes{};
   const std::false_type no{};
+  bool stores_pending = false;                   // the previous tile stored all 32 of its blocks per wave
   for (int r = 0;; ++r) {
-    front(st0, yes, no, 0);                      // stage 0 (first half): starts the sums
+    front(st0, yes, no, 0, stores_pending);      // stage 0 (first half): starts the sums
     int kb = 0;
     for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
       back(st0, st1, kb + 2, kb + 1, ckb0, csb);
@@ -706,6 +711,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
       }
     }
     if (!more) break;
+    // an interior tile issued exactly 32 stores per wave after the DMA of the
+    // next tile's stage 1; vector memory completes in issue order, so the
+    // next tile's first wait can leave those stores in flight
+    stores_pending = ct0 + kLT <= p.T && cn0 + kLN <= p.N;
     cg = ng;
     ct0 = nt0;
     cn0 = nn0;
