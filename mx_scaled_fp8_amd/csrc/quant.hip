@@ -279,8 +279,6 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
 // A token whose position is outside [0, max_pos) gets BF16 NaN (0x7FC0) in
 // its rotated dims; the other dims pass through.
 
-constexpr int kCopyUnroll = 4;                   // chunks per lane of the copying inverse RoPE
-
 struct RopeArgs {
   const uint4* x;             // [T, L] BF16 as 16-byte chunks
   uint4* out;                 // [T, L]
@@ -346,43 +344,25 @@ __device__ __forceinline__ void rope_unit_bf16(const RopeArgs& a, uint32_t row, 
 
 template <int STYLE, bool COPY>
 __global__ __launch_bounds__(kThreads) void rope_bf16_kernel(RopeArgs a) {
+  const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.total) return;
+  const uint32_t row = div_u32(i, a.row_div);
+  const uint32_t rem = i - row * a.row_div.d;
+  const uint32_t head = div_u32(rem, a.head_div);
+  const uint32_t hin = rem - head * a.head_div.d;
+  const uint32_t c0 = row * a.row_chunks + head * a.head_chunks + a.rope_chunk0;
   if constexpr (!COPY) {
-    const uint32_t i = blockIdx.x * kThreads + threadIdx.x;
-    if (i >= a.total) return;
-    const uint32_t row = div_u32(i, a.row_div);
-    const uint32_t rem = i - row * a.row_div.d;
-    const uint32_t head = div_u32(rem, a.head_div);
-    const uint32_t hin = rem - head * a.head_div.d;
-    rope_unit_bf16<STYLE>(a, row, row * a.row_chunks + head * a.head_chunks + a.rope_chunk0, hin);
+    rope_unit_bf16<STYLE>(a, row, c0, hin);
   } else {
-    // kCopyUnroll chunks per lane, kThreads apart: the pass-through chunks'
-    // loads are issued together, and every byte is touched once (non-temporal)
-    uint32_t idx[kCopyUnroll], row[kCopyUnroll], hin[kCopyUnroll], c0[kCopyUnroll];
-    v4u_t v[kCopyUnroll];
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      idx[u] = blockIdx.x * (kThreads * kCopyUnroll) + u * kThreads + threadIdx.x;
-      const uint32_t i = min(idx[u], a.total - 1);
-      row[u] = div_u32(i, a.row_div);
-      const uint32_t rem = i - row[u] * a.row_div.d;
-      const uint32_t head = div_u32(rem, a.head_div);
-      hin[u] = rem - head * a.head_div.d;
-      c0[u] = row[u] * a.row_chunks + head * a.head_chunks + a.rope_chunk0;
-      if (hin[u] < a.rope_chunk0) v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(a.x) + i);
+    if (hin < a.rope_chunk0) {
+      a.out[i] = a.x[i];
+      return;
     }
-#pragma unroll
-    for (int u = 0; u < kCopyUnroll; ++u) {
-      if (idx[u] >= a.total) continue;
-      if (hin[u] < a.rope_chunk0) {
-        __builtin_nontemporal_store(v[u], reinterpret_cast<v4u_t*>(a.out) + idx[u]);
-        continue;
-      }
-      const uint32_t s = hin[u] - a.rope_chunk0;  // chunk inside the rotated slice
-      if (STYLE == MX_ROPE_INTERLEAVED) {
-        if ((s & 1) == 0) rope_unit_bf16<STYLE>(a, row[u], c0[u], s >> 1);
-      } else {
-        if (s < a.half_pairs / 8) rope_unit_bf16<STYLE>(a, row[u], c0[u], s);
-      }
+    const uint32_t s = hin - a.rope_chunk0;      // chunk inside the rotated slice
+    if (STYLE == MX_ROPE_INTERLEAVED) {
+      if ((s & 1) == 0) rope_unit_bf16<STYLE>(a, row, c0, s >> 1);
+    } else {
+      if (s < a.half_pairs / 8) rope_unit_bf16<STYLE>(a, row, c0, s);
     }
   }
 }
@@ -474,8 +454,7 @@ mx_status launch_rope_bf16(const void* x, const int64_t* positions, const void* 
     a.row_chunks = static_cast<uint32_t>(L / 8);
     a.rope_chunk0 = static_cast<uint32_t>((D - rope_dim) / 8);
     a.half_pairs = static_cast<uint32_t>(rope_dim / 2);
-    const uint32_t per_block = in_place ? kThreads : kThreads * kCopyUnroll;
-    const uint32_t blocks = (a.total + per_block - 1) / per_block;
+    const uint32_t blocks = (a.total + kThreads - 1) / kThreads;
     if (rope_dim == 0) {
       // nothing rotates: every chunk is copied (no position is read)
       a.rope_chunk0 = a.head_chunks;
