@@ -6,7 +6,7 @@
 // (g, n, 128-K block)), out[t, g, n] = sum_k A*sa * W*sw, in place of the BF16
 // grouped einsum.
 //
-// The contraction runs on v_mfma_scale_f32_16x16x128_f8f6f4: one instruction
+// Small-T kernels run on v_mfma_scale_f32_16x16x128_f8f6f4: one instruction
 // multiplies a 16x128 FP8 tile by a 128x16 FP8 tile, applies one E8M0 scale
 // per lane to each operand, and accumulates in fp32.  Operand layout (checked
 // on the hardware with one-hot inputs): lane l holds row l%16; with q = l/16,
@@ -15,26 +15,34 @@
 // 128-wide scale group covers an instruction's whole K, so for the wo_a GEMM
 // all four lanes of a row pass the same byte and any K order common to both
 // operands is correct; the block-32 GEMM of the MXFP8 linear needs the exact
-// order above.  The weight is the MFMA's
-// first operand and the activation its second, so each lane's four fp32
-// results are four consecutive n of one token: one 8-byte BF16 store.
+// order above.  The weight is the MFMA's first operand and the activation its
+// second, so each lane's four fp32 results are four consecutive n of one
+// token: one 8-byte BF16 store.  The large-tile kernels run on the 32x32x64
+// form of the same instruction (4 x 4 tiles per wave).
 //
 // FNUZ activations: an FNUZ code c times 2^s equals the OCP code c times
 // 2^(s-1) (the FNUZ grid is the OCP grid halved), so FNUZ bytes are fed to
 // the OCP MFMA with their scale byte lowered by one (0xFF stays NaN; 0 cannot
 // go lower and is kept -- the block is then 2x too large, below 2^-119).
 //
-// Two kernels:
-//  * large: 256 (t) x 256 (n) tiles, 4 waves of 128x128, K-steps of 128.  A
-//    and W tiles go global -> LDS by LDS-DMA (global_load_lds_dwordx4, no
-//    VGPR staging) into a 2-stage ring; 16-byte chunks are XOR-swizzled so
-//    that the MFMA operand reads (two ds_read_b128 per operand) are bank
-//    conflict free.  Tiles are mapped to workgroups XCD-aware: the 8 XCDs
-//    each own a contiguous range of tiles, n fastest, so the n-tiles sharing
-//    one activation panel run together on one XCD's L2.
-//  * small-T (T <= 64, decode and the MXFP8 linear): one workgroup per
-//    (g, 16*NT n) with all T rows; the 4 waves split K and reduce through LDS.
-//    Operands stream straight from global memory (weight-bandwidth bound).
+// Kernels:
+//  * bmm_large_kernel / bmm_persistent_kernel (T > 64): 256 (t) x 256 (n)
+//    tiles, 4 waves of 128x128, K-steps of 128.  A and W tiles go global ->
+//    LDS by LDS-DMA (global_load_lds_dwordx4, no VGPR staging) into a 2-stage
+//    ring; 16-byte chunks are XOR-swizzled so that the MFMA operand reads
+//    (two ds_read_b128 per operand) are bank conflict free.  Tiles are mapped
+//    to workgroups XCD-aware: the 8 XCDs each own a contiguous range of
+//    tiles, n fastest, so the n-tiles sharing one activation panel run
+//    together on one XCD's L2.  The persistent kernel (K = 2048 or 4096)
+//    keeps one workgroup per compute unit and runs the stage pipeline across
+//    tile boundaries.
+//  * bmm_decode_kernel (T <= 64, K of 1024 to 8192): one workgroup per
+//    (g, 64 n) with all T rows; both operands through an LDS-DMA ring of 8
+//    K-steps; the waves split n.  A BF16 mode serves the BF16 arm.
+//  * bmm_small_kernel (T <= 64, other K): the 4 waves split K, operands
+//    double-buffered in registers, partial sums reduced through LDS.
+//  * gemm_mx32_dma_kernel / gemm_mx32_dma1_kernel: the MXFP8 linear's
+//    block-32 GEMM (M <= 64 / M <= 16) on the decode kernel's ring.
 #include <algorithm>
 #include <type_traits>
 
