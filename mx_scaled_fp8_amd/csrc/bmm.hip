@@ -748,11 +748,11 @@ constexpr int kSmallWaves = 4;
 constexpr int kSmallThreads = 64 * kSmallWaves;
 
 // One workgroup: all T (<= 64) rows x 16*NT columns n of one group g, kSmallWaves
-// waves (two per SIMD).  Wave w takes K-steps w, w+kSmallWaves, ...; partial
-// sums meet in LDS.  The workgroup's scale
-// rows are staged in LDS once (W rows n0.. are one contiguous block; A rows
-// one per token), so the loop reads only operand bytes from memory; the
-// operands of a wave's next K-step are loaded while the current one's MFMAs run.
+// waves.  Wave w takes K-steps w, w+kSmallWaves, ...; partial sums meet in
+// LDS.  The workgroup's scale rows are staged in LDS once (W rows n0.. are one
+// contiguous block; A rows one per token), so the loop reads only operand
+// bytes from memory; the operands of a wave's next K-step are loaded while the
+// current one's MFMAs run.
 template <int NT, int SB, bool A_FNUZ>
 __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
   __shared__ float red[4][NT * 4][4][64];   // [wave % 4][tile][reg][lane]
