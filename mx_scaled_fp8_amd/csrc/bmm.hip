@@ -507,35 +507,57 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     }
   };
 
-  // ---- scales: thread tid owns W row tid and A row tid of a tile; slot s of
-  // a buffer holds stage s (loop stage kb reads slot (kb + kb0) mod KB)
+  // ---- scales: a slot holds one stage's 4-byte words [operand][wave half]
+  // [row % 32] (tile bytes 0..3); slot s of a buffer holds stage s (loop
+  // stage kb reads slot (kb + kb0) mod KB).  Thread tid builds the words of
+  // operand tid/128, wave half (tid/64)%2, row tid%32 for half of the stages,
+  // (tid/32)%2: it loads that stage range of the 4 rows (one per tile) and
+  // transposes their bytes into words, so that each word is one LDS store.
   constexpr int kScStep = 2 * 2 * 32 * 4;
-  constexpr int kScOp = 2 * 32 * 4;
   constexpr int kScBuf = kScaleWin * kScStep;
-  uint8_t* const sc_dst = &lds_sc[0][0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
-  uint4 lw0, lw1, la0, la1;
-  auto load_scales = [&](int g, int t0, int n0) {   // into registers; KB bytes per row
-    const uint8_t* sW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, p.N - 1 - n0)) * KB;
-    const uint8_t* sA = p.sa + (static_cast<size_t>(t0 + min(tid, p.T - 1 - t0)) * p.G + g) * KB;
-    lw0 = *reinterpret_cast<const uint4*>(sW);
-    la0 = *reinterpret_cast<const uint4*>(sA);
-    lw1 = make_uint4(0, 0, 0, 0);
-    la1 = lw1;
-    if (KB > 16) {
-      lw1 = *reinterpret_cast<const uint4*>(sW + 16);
-      la1 = *reinterpret_cast<const uint4*>(sA + 16);
+  const int sc_op = tid >> 7, sc_half = (tid >> 6) & 1, sc_sh = (tid >> 5) & 1, sc_r = tid & 31;
+  uint8_t* const sc_dst = &lds_sc[0][0][sc_op][sc_half][sc_r][0] + sc_sh * (KB / 2) * kScStep;
+  uint4 lr[4];                                   // rows of tiles 0..3: stages [sc_sh*KB/2, +KB/2)
+  auto load_scales = [&](int g, int t0, int n0) {   // into registers
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = sc_half * 128 + i * 32 + sc_r;
+      const uint8_t* src = sc_op == 0
+          ? p.sw + (static_cast<size_t>(g) * p.N + n0 + min(row, p.N - 1 - n0)) * KB + sc_sh * (KB / 2)
+          : p.sa + (static_cast<size_t>(t0 + min(row, p.T - 1 - t0)) * p.G + g) * KB + sc_sh * (KB / 2);
+      if (KB > 16) {
+        lr[i] = *reinterpret_cast<const uint4*>(src);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(src);
+        lr[i] = make_uint4(v.x, v.y, 0, 0);
+      }
     }
   };
   auto store_scales = [&](int sb) {              // registers -> LDS buffer sb
     uint8_t* dst = sc_dst + sb * kScBuf;
-    const uint32_t ww[8] = {lw0.x, lw0.y, lw0.z, lw0.w, lw1.x, lw1.y, lw1.z, lw1.w};
-    const uint32_t aw[8] = {la0.x, la0.y, la0.z, la0.w, la1.x, la1.y, la1.z, la1.w};
 #pragma unroll
-    for (int s = 0; s < kScaleWin; ++s) {        // slots past the last stage are never read
-      const int bw = static_cast<int>((ww[s >> 2] >> (8 * (s & 3))) & 0xFF);
-      const int ba = static_cast<int>((aw[s >> 2] >> (8 * (s & 3))) & 0xFF);
-      dst[s * kScStep] = static_cast<uint8_t>(bw);
-      dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(ba) : ba);
+    for (int k = 0; k < 4; ++k) {                // dword k of each row: stages 4k..4k+3 of the range
+      if (k >= KB / 8) break;
+      uint32_t r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r[i] = k == 0 ? lr[i].x : k == 1 ? lr[i].y : k == 2 ? lr[i].z : lr[i].w;
+        if (A_FNUZ && sc_op == 1) {              // FNUZ activation scales -> OCP scales, per byte
+          uint32_t o = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) o |= static_cast<uint32_t>(fnuz_scale_to_ocp((r[i] >> (8 * b)) & 0xFF)) << (8 * b);
+          r[i] = o;
+        }
+      }
+      // 4 x 4 byte transpose: word j = byte j of rows 0, 1, 2, 3
+      const uint32_t t0 = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);   // r0b0 r1b0 r0b1 r1b1
+      const uint32_t t1 = __builtin_amdgcn_perm(r[3], r[2], 0x05010400u);   // r2b0 r3b0 r2b1 r3b1
+      const uint32_t t2 = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);   // r0b2 r1b2 r0b3 r1b3
+      const uint32_t t3 = __builtin_amdgcn_perm(r[3], r[2], 0x07030602u);   // r2b2 r3b2 r2b3 r3b3
+      const uint32_t w[4] = {__builtin_amdgcn_perm(t1, t0, 0x05040100u), __builtin_amdgcn_perm(t1, t0, 0x07060302u),
+                             __builtin_amdgcn_perm(t3, t2, 0x05040100u), __builtin_amdgcn_perm(t3, t2, 0x07060302u)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint32_t*>(dst + (4 * k + j) * kScStep) = w[j];
     }
   };
   auto read_scales = [&](int kb, int kb0, int sb, uint32_t& swv, uint32_t& sav) {
