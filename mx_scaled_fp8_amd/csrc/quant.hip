@@ -209,6 +209,7 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     p = a.pos[row];
     ok = p >= 0 && p < a.max_pos;
   }
+  uint32_t sword = 0;                   // group 128: the scale bytes of this row's 4 groups
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t c = cidx[u];
@@ -251,11 +252,27 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
       codes = make_uint2(nan4, nan4);
     }
     const uint32_t craw = base + u * 16;
+    const uint32_t sbyte = finite ? static_cast<uint32_t>(e + 127) : 0xFFu;
+    if constexpr (GROUP == 128) sword |= sbyte << (8 * u);
     if (craw < a.total_chunks) {
       const v2u_t cw = {codes.x, codes.y};
       __builtin_nontemporal_store(cw, reinterpret_cast<v2u_t*>(a.q) + craw);
-      if ((threadIdx.x & (kLanesPerGroup - 1)) == 0)
-        a.scale[craw / kLanesPerGroup] = finite ? static_cast<uint8_t>(e + 127) : uint8_t(0xFF);
+      if (GROUP != 128 && (threadIdx.x & (kLanesPerGroup - 1)) == 0)
+        a.scale[craw / kLanesPerGroup] = static_cast<uint8_t>(sbyte);
+    }
+  }
+  if constexpr (GROUP == 128) {
+    // a row of 16 lanes quantised the 4 consecutive groups of its segment:
+    // their scale bytes leave as one 4-byte store
+    if ((threadIdx.x & 15) == 0) {
+      uint8_t* dst = a.scale + base / 16;
+      if (base + 48 < a.total_chunks && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+        *reinterpret_cast<uint32_t*>(dst) = sword;
+      } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+          if (base + u * 16 < a.total_chunks) dst[u] = static_cast<uint8_t>(sword >> (8 * u));
+      }
     }
   }
 }

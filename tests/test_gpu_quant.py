@@ -80,6 +80,28 @@ def test_ragged_rows(tables, T):
     assert_codes_close(q, rq, s, rs, F.OCP, exact=True, what=f"T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 7, 33])
+def test_rows_not_a_multiple_of_512_and_unaligned_scales(tables, T):
+    """H*D = 384: a lane row's 4 groups straddle token rows and the last one
+    can be partial; the scale output starts 1 byte past an aligned address
+    (the 4-byte scale store then falls back to bytes)."""
+    rng = np.random.default_rng(50 + T)
+    H, D = 3, 128
+    x = workloads.activations(rng, T, H * D)
+    pos = rng.integers(0, 8192, T)
+    cos, sin, dcos, dsin = tables
+    say("quant H*D=384 unaligned scales", T)
+    q = torch.empty((T, H * D), dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((T * H * D // 128 + 8,), 0xAA, dtype=torch.uint8, device="cuda")
+    s = sbuf[1:1 + T * H * D // 128].view(T, H * D // 128)
+    mx.mx_inv_rope_group_quant(dev_u16(x), dev_i64(pos), dcos, dsin, H, D, 64, q=q, scale=s)
+    torch.cuda.synchronize()
+    rq, rs = inv_rope_group_quant(x, pos, cos, sin, H, D, 64)
+    assert_codes_close(host_u8(q), rq, host_u8(s), rs, F.OCP, exact=False, what=f"T={T}")
+    out = host_u8(sbuf)
+    assert out[0] == 0xAA and np.all(out[1 + T * H * D // 128:] == 0xAA)    # nothing written outside
+
+
 def test_empty(tables):
     _, _, dcos, dsin = tables
     x = torch.empty((0, 512), dtype=torch.int16, device="cuda")
