@@ -7,14 +7,16 @@ GEMM.  Inputs are seeded synthetic tensors resident in HBM before the timed
 region.  The headline value is the GEMM's FLOPs per step (2*T*G*N*K) divided
 by the step time, in TFLOP/s.
 
-Printed: one JSON line (the headline, with `roofline` for the GEMM --
-measured with HIP events on the stream the kernels run on -- and
-`cpu_baseline`, the CPU oracle timed on a bounded sample of the same
-workload), followed by secondary per-kernel records on stderr unless
---json-extra is given, in which case they are folded into the JSON line.
+Printed: one JSON line -- the headline, with `roofline` for the GEMM
+(measured with HIP events on the stream the kernels run on) and
+`cpu_baseline` (the CPU oracle timed on a bounded sample of the same
+workload).  --extra adds `kernels` (decode batch, MXFP8 linear, dequant,
+the production down_proj, the BF16 arm, 40-call graph timings) and --long
+adds the 100,000-token chunked prefill, both inside the same line; progress
+goes to stderr.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--extra] [--long]
+                       [--cpu-tokens N] [--extra] [--long] [--copy-calibration]
 """
 
 import argparse
