@@ -156,3 +156,49 @@ def test_down_proj_production_shares(shards, tp, M):
     else:
         out = host_u16(mx.mx_linear(dx, dw, dws))
         assert_gemm_close(out, ref, f"TP{tp} K={K} M={M} fp8")
+
+
+# Every shape class of the block-scaled branch's weight-resident GEMM: 1..16
+# rows (the waves split K into quarters; some quarters empty when K / 128 < 4
+# or ragged), 17..64 rows (one token tile per wave, K / 128 up to 18), and the
+# ring kernel beyond that (K / 128 = 19, 32).  N = 48: three workgroups.
+WRES_CASES = [(1, 1), (7, 2), (16, 3), (1, 4), (5, 5), (16, 9), (3, 13), (16, 18), (9, 29), (1, 33), (16, 48),
+              (2, 61), (16, 64), (17, 1), (40, 2), (64, 5), (33, 9), (64, 17), (17, 18), (64, 18), (40, 19),
+              (64, 32)]
+
+
+@pytest.mark.parametrize("M,KB", WRES_CASES)
+def test_linear_fp8_row_and_k_classes(M, KB):
+    K, N = 128 * KB, 48
+    rng = np.random.default_rng(1000 * M + KB)
+    x = workloads.activations(rng, M, K)
+    w = workloads.weight_codes(rng, (N, K))
+    ws = workloads.scale_bytes(rng, (N, K // 32), -10, -4)
+    say("mx_linear fp8 shape class", M, K)
+    # rows past M of the output buffer must stay untouched
+    big = torch.full((M + 3, N), -7.0, dtype=torch.bfloat16, device="cuda")
+    mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws), out=big[:M])
+    got = host_u16(big)
+    assert np.all(got[M:] == host_u16(torch.full((1,), -7.0, dtype=torch.bfloat16)).item())
+    assert_gemm_close(got[:M], G.mx_linear(x, w, ws, 32), f"M={M} K={K}")
+
+
+@pytest.mark.parametrize("M,KB", [(5, 9), (64, 18), (16, 40)])
+def test_linear_fp8_nan_blocks(M, KB):
+    """A NaN in x gives its block NaN codes and the 0xFF scale, so the whole
+    output row is NaN; a 0xFF weight scale makes its output column NaN; the
+    rest stays within the bound."""
+    K, N = 128 * KB, 48
+    rng = np.random.default_rng(77 + M)
+    x = workloads.activations(rng, M, K)
+    x[M - 1, 37] = 0x7FC0                       # BF16 NaN in the last row
+    w = workloads.weight_codes(rng, (N, K))
+    ws = workloads.scale_bytes(rng, (N, K // 32), -10, -4)
+    ws[21, K // 32 - 1] = 0xFF
+    say("mx_linear fp8 NaN blocks", M, K)
+    got = host_u16(mx.mx_linear(dev_u16(x), dev_u8(w), dev_u8(ws)))
+    ref = G.mx_linear(x, w, ws, 32)
+    nan = np.isnan(ref)
+    assert nan[M - 1].all() and nan[:, 21].all() and nan.sum() == N + M - 1
+    assert np.array_equal(np.isnan(F.bf16_to_f64(got)), nan)
+    assert_gemm_close(got[~nan], ref[~nan], f"M={M} K={K} finite part")
