@@ -20,6 +20,8 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
                      void* out, int64_t T, int32_t G, int32_t N, int32_t K, hipStream_t stream);
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+bool launch_linear_mx32_fused(const void* x, const uint8_t* w, const uint8_t* sw, void* out, int64_t M, int64_t N,
+                              int64_t K, hipStream_t stream, mx_status* st);
 bool launch_gemm_mx32_wres(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream, mx_status* st);
 mx_status launch_gemm_bf16(const void* x, const void* w, void* out, int64_t M, int64_t N, int64_t K,
@@ -331,13 +333,15 @@ mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const ui
     // x -> MXFP8 (OCP, block 32, no rotation) into the workspace, then the
     // block-scaled FP8 GEMM
     count(C_LINEAR_FP8);
-    uint8_t* xq = static_cast<uint8_t*>(workspace);
-    uint8_t* xs = xq + (static_cast<size_t>(M) * K + 15) / 16 * 16;
-    st = launch_quant(x, nullptr, nullptr, nullptr, 0, M, 1, static_cast<int32_t>(K), 0, MX_ROPE_INTERLEAVED,
-                      MX_LINEAR_BLOCK, MX_FP8_E4M3_OCP, xq, xs, s);
-    if (st == MX_OK &&
-        !launch_gemm_mx32_wres(xq, xs, static_cast<const uint8_t*>(w), w_scale, out, M, N, K, s, &st))
-      st = launch_gemm_mx32(xq, xs, static_cast<const uint8_t*>(w), w_scale, out, M, N, K, s);
+    const uint8_t* w8 = static_cast<const uint8_t*>(w);
+    if (!launch_linear_mx32_fused(x, w8, w_scale, out, M, N, K, s, &st)) {
+      uint8_t* xq = static_cast<uint8_t*>(workspace);
+      uint8_t* xs = xq + (static_cast<size_t>(M) * K + 15) / 16 * 16;
+      st = launch_quant(x, nullptr, nullptr, nullptr, 0, M, 1, static_cast<int32_t>(K), 0, MX_ROPE_INTERLEAVED,
+                        MX_LINEAR_BLOCK, MX_FP8_E4M3_OCP, xq, xs, s);
+      if (st == MX_OK && !launch_gemm_mx32_wres(xq, xs, w8, w_scale, out, M, N, K, s, &st))
+        st = launch_gemm_mx32(xq, xs, w8, w_scale, out, M, N, K, s);
+    }
   } else {
     // an FP8 weight with K % 128 != 0 that was not prepared at load: dequantise
     // it into the workspace on this call; it never reaches the scaled GEMM
