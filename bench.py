@@ -20,9 +20,11 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 import argparse
+import ctypes
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -78,6 +80,28 @@ class Timer:
         e = self.torch.cuda.Event(enable_timing=True)
         e.record(self.stream)
         return e
+
+
+def run_env(torch):
+    """Device, clocks and software versions the numbers were taken with."""
+    prop = torch.cuda.get_device_properties(0)
+    env = {"device": torch.cuda.get_device_name(0), "arch": getattr(prop, "gcnArchName", None),
+           "compute_units": prop.multi_processor_count, "hbm_GiB": round(prop.total_memory / 2**30, 1),
+           "max_sclk_MHz": None, "torch": torch.__version__, "hip": torch.version.hip, "git": None}
+    try:
+        env["git"] = subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=os.path.dirname(os.path.abspath(__file__)),
+                                    capture_output=True, text=True, timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        # the runtime's peak shader clock (hipDeviceAttributeClockRate, in kHz)
+        hip = ctypes.CDLL("libamdhip64.so")
+        khz = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), 5, torch.cuda.current_device()) == 0:
+            env["max_sclk_MHz"] = khz.value // 1000
+    except OSError:
+        pass
+    return env
 
 
 def bench_prefill(mx, torch, workloads, steps, warmup, fmt=0):
@@ -524,6 +548,7 @@ def main():
                      "launch_us": round(b_avg_ms * 1e3, 2), "algorithmic_flops": p.flops,
                      "algorithmic_bytes": bmm_bytes(p.T, p.G, p.N, p.K)},
         "wall_s_timed_region": round(r["wall_s"], 4),
+        "env": run_env(torch),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle on {args.cpu_tokens} tokens")

@@ -14,6 +14,11 @@
 * The pages' production layer, the shared expert's down_proj (N = 5120) at
   each tensor-parallel share of K = 2304 (TP1/2/4/8: K = 2304, 1152, 576,
   288), decode batches of 1 and 8 rows: every branch the K allows.
+* Every row/K class of the block-scaled kernels (x quantised inside the GEMM
+  for up to 16 rows; the weight-resident GEMM; the ring kernels beyond), rows
+  past M left untouched, NaN blocks on either operand.
+* The identity as the FP8 weight makes each output one dequantised x code:
+  the codes and scales made for x are checked bit for bit against the oracle.
 """
 
 import numpy as np
@@ -202,3 +207,31 @@ def test_linear_fp8_nan_blocks(M, KB):
     assert nan[M - 1].all() and nan[:, 21].all() and nan.sum() == N + M - 1
     assert np.array_equal(np.isnan(F.bf16_to_f64(got)), nan)
     assert_gemm_close(got[~nan], ref[~nan], f"M={M} K={K} finite part")
+
+
+@pytest.mark.parametrize("M,K", [(1, 128), (5, 1152), (16, 2304), (9, 4096), (40, 1152), (64, 2304)])
+def test_linear_fp8_identity_weight_returns_quantised_x(M, K):
+    """With the identity as the FP8 weight (code 0x38 = 1.0 on the diagonal,
+    unit scales) every output is one dequantised x code, which BF16 holds
+    exactly.  So the codes and scales this branch makes for x -- inside the
+    GEMM for up to 16 rows, by the quantiser otherwise -- are checked bit for
+    bit against the oracle's, on random BF16 bit patterns (magnitudes from
+    2^-63 to 2^124, both signs) with one all-zero block per row."""
+    from oracle.quant import group_quant
+    rng = np.random.default_rng(M * 7919 + K)
+    sign = rng.integers(0, 2, (M, K)).astype(np.uint16) << 15
+    x = (sign | (rng.integers(64, 251, (M, K)).astype(np.uint16) << 7) | rng.integers(0, 128, (M, K)).astype(np.uint16))
+    zero_block = rng.integers(0, K // 32, M)
+    for m in range(M):
+        x[m, 32 * zero_block[m]: 32 * zero_block[m] + 32] = 0
+    w = np.zeros((K, K), np.uint8)
+    w[np.arange(K), np.arange(K)] = 0x38
+    ws = np.full((K, K // 32), 127, np.uint8)
+    say("mx_linear fp8 identity weight", M, K)
+    got = host_u16(mx.mx_linear(dev_u16(x.astype(np.uint16)), dev_u8(w), dev_u8(ws)))
+    xq, xs = group_quant(x, 32, F.OCP)
+    ref = F.f64_to_bf16_rne(G.scaled_operand(xq, xs, 32, F.OCP))
+    # a zero sum is +0 on the GPU (the accumulator starts at +0)
+    ref = np.where(ref == 0x8000, 0, ref).astype(np.uint16)
+    got = np.where(got == 0x8000, 0, got).astype(np.uint16)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} of {ref.size} outputs differ"
