@@ -34,8 +34,8 @@
 //    to workgroups XCD-aware: the 8 XCDs each own a contiguous range of
 //    tiles, n fastest, so the n-tiles sharing one activation panel run
 //    together on one XCD's L2.  The persistent kernel (K = 2048 or 4096)
-//    keeps one workgroup per compute unit and runs the stage pipeline across
-//    tile boundaries.
+//    keeps one workgroup per compute unit, runs the stage pipeline across
+//    tile boundaries and stores each tile through LDS as 128-byte row pieces.
 //  * bmm_decode_kernel (T <= 64, K of 1024 to 8192): one workgroup per
 //    (g, 64 n) with all T rows; both operands through an LDS-DMA ring of 8
 //    K-steps; the waves split n.  A BF16 mode serves the BF16 arm.
@@ -445,6 +445,19 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
 // Requires K / 128 in {16, 32} (an even number of stages, all scales of a
 // tile in one window) and 16-byte aligned scale tensors; other shapes use
 // bmm_large_kernel.
+// calls f(integral_constant<int, k>) for k = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+// the order of the 16 MFMAs of a half-stage (W tile I, A tile J): each
+// fragment is first used as late as the read order below allows
+constexpr int kOrdI[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+constexpr int kOrdJ[16] = {0, 1, 0, 1, 2, 2, 0, 1, 2, 3, 3, 3, 0, 1, 2, 3};
+
 template <bool A_FNUZ>
 __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
@@ -456,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   const int slot = blockIdx.x >> 3;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wt = wave >> 1;
   const int KB = p.K / kBK;                    // 16 or 32
   const uint32_t rowA = static_cast<uint32_t>(p.G) * p.K;
@@ -490,7 +503,11 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // ---- DMA of one tile's stages (the tile whose stages are being fetched)
   const int dma_row = wave * 8 + (lane >> 3);
   const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz8(dma_row)) * 16;
-  uint32_t offW[8], offA[8];
+  // lane's byte offset in its first row group; row groups it = 1..7 add
+  // it * 32 rows, and rows past N or T are clamped to the last row (re-read)
+  const uint32_t baseW = static_cast<uint32_t>(dma_row) * static_cast<uint32_t>(p.K) + dma_chunk;
+  const uint32_t baseA = static_cast<uint32_t>(dma_row) * rowA + dma_chunk;
+  uint32_t capW, capA;
   const uint8_t* dW;
   const uint8_t* dA;
   int dkb0;
@@ -498,13 +515,8 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     dW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
     dA = p.a + static_cast<size_t>(t0) * rowA + static_cast<size_t>(g) * p.K;
     dkb0 = kb0;
-    const int limW = p.N - 1 - n0, limA = p.T - 1 - t0;   // rows past N or T re-read the last row
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int r = it * 32 + dma_row;
-      offW[it] = static_cast<uint32_t>(min(r, limW)) * static_cast<uint32_t>(p.K) + dma_chunk;
-      offA[it] = static_cast<uint32_t>(min(r, limA)) * rowA + dma_chunk;
-    }
+    capW = static_cast<uint32_t>(p.N - 1 - n0) * static_cast<uint32_t>(p.K) + dma_chunk;
+    capA = static_cast<uint32_t>(p.T - 1 - t0) * rowA + dma_chunk;
   };
   auto issue = [&](uint8_t* buf, int kb) {   // kb < KB
     int kr = kb + dkb0;
@@ -514,8 +526,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int rb = it * 32 + wave * 8;
-      __builtin_amdgcn_global_load_lds(bW + offW[it], (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(bA + offA[it], (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
+      const uint32_t oW = min(baseW + static_cast<uint32_t>(it * 32) * static_cast<uint32_t>(p.K), capW);
+      const uint32_t oA = min(baseA + static_cast<uint32_t>(it * 32) * rowA, capA);
+      __builtin_amdgcn_global_load_lds(bW + oW, (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bA + oA, (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
     }
   };
 
@@ -604,25 +618,6 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     w[3] = read_frag(qw + 96 * kBK, c0, c1);
   };
   v16f acc[4][4];
-  auto mma_half = [&](const v8i (&w)[4], const v8i (&a)[4], uint32_t swv, uint32_t sav, auto first) {
-    constexpr bool F = decltype(first)::value;
-    mfma_ij<0, 0, F>(acc, w, a, swv, sav);
-    mfma_ij<0, 1, F>(acc, w, a, swv, sav);
-    mfma_ij<1, 0, F>(acc, w, a, swv, sav);
-    mfma_ij<1, 1, F>(acc, w, a, swv, sav);
-    mfma_ij<0, 2, F>(acc, w, a, swv, sav);
-    mfma_ij<1, 2, F>(acc, w, a, swv, sav);
-    mfma_ij<2, 0, F>(acc, w, a, swv, sav);
-    mfma_ij<2, 1, F>(acc, w, a, swv, sav);
-    mfma_ij<2, 2, F>(acc, w, a, swv, sav);
-    mfma_ij<0, 3, F>(acc, w, a, swv, sav);
-    mfma_ij<1, 3, F>(acc, w, a, swv, sav);
-    mfma_ij<2, 3, F>(acc, w, a, swv, sav);
-    mfma_ij<3, 0, F>(acc, w, a, swv, sav);
-    mfma_ij<3, 1, F>(acc, w, a, swv, sav);
-    mfma_ij<3, 2, F>(acc, w, a, swv, sav);
-    mfma_ij<3, 3, F>(acc, w, a, swv, sav);
-  };
   auto pin_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -639,19 +634,51 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // stage rs_kb (rotation rs_kb0, buffer rs_sb) with the first half of the
   // next stage from `nxt`.
   uint32_t swv, sav;
+  // Step k of a half-stage: MFMA k (in kOrdI/kOrdJ order), fragment read k
+  // of the other half (k < 8, in read order), and in back() DMA instruction
+  // k.  Each step is fenced with a scheduling barrier, so the compiler keeps
+  // this one-to-one interleave; left to itself it bunched the DMA at the end
+  // of the half once the DMA addresses no longer went through VGPRs.
+  auto mfma_k = [&](auto K, const v8i (&w)[4], const v8i (&a)[4], auto first) {
+    constexpr int k = decltype(K)::value;
+    mfma_ij<kOrdI[k], kOrdJ[k], decltype(first)::value>(acc, w, a, swv, sav);
+  };
+  auto read_k = [&](auto K, const uint8_t* buf, int c0, int c1, v8i (&w)[4], v8i (&a)[4]) {
+    constexpr int k = decltype(K)::value;   // read order: w0 a0 a1 w1 a2 w2 a3 w3
+    constexpr bool isW = k == 0 || k == 3 || k == 5 || k == 7;
+    constexpr int idx = k == 0 ? 0 : k == 1 ? 0 : k == 2 ? 1 : k == 3 ? 1 : k == 4 ? 2 : k == 5 ? 2 : 3;
+    if constexpr (isW)
+      w[idx] = read_frag(buf + rdW + idx * 32 * kBK, c0, c1);
+    else
+      a[idx] = read_frag(buf + rdA + idx * 32 * kBK, c0, c1);
+  };
+  auto dma_k = [&](auto K, uint8_t* buf, const uint8_t* bW, const uint8_t* bA) {
+    constexpr int k = decltype(K)::value, it = k >> 1;
+    const int rb = it * 32 + wave * 8;
+    if constexpr ((k & 1) == 0) {
+      uint32_t b = baseW;
+      // opaque copy: the offsets are formed here rather than hoisted out of
+      // the loop as 16 precomputed 64-bit addresses (32 VGPRs)
+      asm volatile("" : "+v"(b));
+      const uint32_t oW = min(b + static_cast<uint32_t>(it * 32) * static_cast<uint32_t>(p.K), capW);
+      __builtin_amdgcn_global_load_lds(bW + oW, (lds_void_t*)(buf + rb * kBK), 16, 0, 0);
+    } else {
+      uint32_t b = baseA;
+      asm volatile("" : "+v"(b));
+      const uint32_t oA = min(b + static_cast<uint32_t>(it * 32) * rowA, capA);
+      __builtin_amdgcn_global_load_lds(bA + oA, (lds_void_t*)(buf + kOpBytes + rb * kBK), 16, 0, 0);
+    }
+  };
   // front(cur, first, with_scales): `first` starts the tile's sums;
   // `with_scales` also writes the next tile's staged scales (load_scales) to
   // LDS buffer `scale_sb` before the barrier, so they are visible after it.
   auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb, bool stores_pending = false) {
     __builtin_amdgcn_sched_barrier(0);
-    mma_half(fw[0], fa[0], swv, sav, first);
-    read_half(cur, ch10, ch11, fw[1], fa[1]);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    static_for<0, 16>([&](auto K) {
+      mfma_k(K, fw[0], fa[0], first);
+      if constexpr (decltype(K)::value < 8) read_k(K, cur, ch10, ch11, fw[1], fa[1]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     if (stores_pending)
@@ -670,21 +697,17 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     // wait for it
     uint32_t swv1, sav1;
     read_scales(rs_kb, rs_kb0, rs_sb, swv1, sav1);
-    issue(cur, dma_kb);
-    mma_half(fw[1], fa[1], swv, sav, std::false_type{});
-    read_half(nxt, ch00, ch01, fw[0], fa[0]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // the two scale reads
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one DMA per MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+    int kr = dma_kb + dkb0;
+    kr -= kr >= KB ? KB : 0;
+    const uint8_t* bW = dW + static_cast<uint32_t>(kr) * kBK;
+    const uint8_t* bA = dA + static_cast<uint32_t>(kr) * kBK;
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 16>([&](auto K) {
+      mfma_k(K, fw[1], fa[1], std::false_type{});
+      dma_k(K, cur, bW, bA);
+      if constexpr (decltype(K)::value < 8) read_k(K, nxt, ch00, ch01, fw[0], fa[0]);
+      __builtin_amdgcn_sched_barrier(0);
+    });
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
     swv = swv1;
@@ -732,23 +755,59 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     front(st1, no, yes, csb ^ 1);                // waits for it and for the scale loads; stages the scales
     back(st1, st0, 1, 0, nkb0, csb ^ 1);         // next tile's stage 1 -> st1; its stage 0 half 0
 
-    // epilogue of this tile, straight from the accumulators (see bmm_large_kernel)
+    // epilogue of this tile.  In the accumulator layout a lane holds one
+    // token and two lanes share a row, so a direct store writes 32 bytes per
+    // row; instead each 32-row x 64-column piece of the wave's sub-tile goes
+    // through LDS (this tile's scale buffer, free since the transition
+    // barrier; 4 KiB per wave) and leaves as 8 rows x 128 bytes per store.
+    {
+      uint8_t* const stg = &lds_sc[csb][0][0][0][0][0] + wave * 4096;
+      const int lr = lane >> 3, lc = lane & 7;     // read side: row in group of 8, 16-byte chunk
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = ct0 + wt * 128 + j * 32 + r32;
-      uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + cg) * p.N;
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v16f& v = acc[i][j];
+        for (int ip = 0; ip < 2; ++ip) {
 #pragma unroll
-        for (int pp = 0; pp < 2; ++pp) {
-          const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
-          const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
-          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-          const int n = cn0 + wn * 128 + i * 32 + pp * 16 + q2 * 8;
-          if (t < p.T && n < p.N)
-            *reinterpret_cast<uint4*>(orow + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+          for (int ii = 0; ii < 2; ++ii) {
+            const v16f& v = acc[2 * ip + ii][j];
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+              const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+              const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+              const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+              const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+              const int c = ii * 4 + pp * 2 + q2;   // 16-byte chunk of the 128-byte row piece
+              const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg)) + r32 * 128 + ((c ^ (r32 & 7)) << 4);
+              typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+              const v4u_t dv = {s0[0], s1[0], s0[1], s1[1]};
+              asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(dv) : "memory");
+            }
+          }
+          typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+          v4u_t d0, d1, d2, d3;
+          {
+            const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg)) + lr * 128 + ((lc ^ lr) << 4);
+            // rows lr, 8 + lr, 16 + lr, 24 + lr (row & 7 == lr for all four)
+            asm volatile(
+                "s_waitcnt lgkmcnt(0)\n"
+                "ds_read_b128 %0, %4\n"
+                "ds_read_b128 %1, %4 offset:1024\n"
+                "ds_read_b128 %2, %4 offset:2048\n"
+                "ds_read_b128 %3, %4 offset:3072\n"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+                : "v"(a)
+                : "memory");
+          }
+          const uint4 d[4] = {make_uint4(d0[0], d0[1], d0[2], d0[3]), make_uint4(d1[0], d1[1], d1[2], d1[3]),
+                              make_uint4(d2[0], d2[1], d2[2], d2[3]), make_uint4(d3[0], d3[1], d3[2], d3[3])};
+#pragma unroll
+          for (int sg = 0; sg < 4; ++sg) {
+            const int t = ct0 + wt * 128 + j * 32 + sg * 8 + lr;
+            const int n = cn0 + wn * 128 + ip * 64 + lc * 8;
+            if (t < p.T && n < p.N)
+              *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + cg) * p.N + n) = d[sg];
+          }
         }
       }
     }
