@@ -35,7 +35,8 @@
 //    tiles, n fastest, so the n-tiles sharing one activation panel run
 //    together on one XCD's L2.  The persistent kernel (K = 2048 or 4096)
 //    keeps one workgroup per compute unit, runs the stage pipeline across
-//    tile boundaries and stores each tile through LDS as 128-byte row pieces.
+//    tile boundaries and stores each tile through LDS as 128-byte row pieces
+//    while the next tile's first MFMAs run.
 //  * bmm_decode_kernel (T <= 64, K of 1024 to 8192): one workgroup per
 //    (g, 64 n) with all T rows; both operands through an LDS-DMA ring of 8
 //    K-steps; the waves split n.  A BF16 mode serves the BF16 arm.
@@ -441,10 +442,11 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
 // from round to round, see tile_at).  The next tile's stages 0 and 1 and its
 // scales are fetched during the current tile's last two stages (scales go to
 // the other of two LDS scale buffers), so the stage pipeline runs through
-// tile boundaries and only the epilogue stores sit between two tiles.
-// Requires K / 128 in {16, 32} (an even number of stages, all scales of a
-// tile in one window) and 16-byte aligned scale tensors; other shapes use
-// bmm_large_kernel.
+// tile boundaries; a tile's epilogue is folded into the first half-stage of
+// the next (front_fold).  Requires K / 128 in {16, 32} (an even number of
+// stages, all scales of a tile in one window) and 16-byte aligned scale
+// tensors; other shapes use bmm_large_kernel.
+
 // calls f(integral_constant<int, k>) for k = B .. E-1, in order
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -482,11 +484,12 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // tile (first t-tile of the round) misses in L2 on every stage, while the
   // tiles behind it find the rows there; with it the leading role moves
   // between compute units from round to round, so no unit falls behind on
-  // all of its tiles (about 3% less time for the launch at T = 8192).  The
-  // K loop of tile (tt, nt) starts at stage 2 (tt + nt) mod KB: tiles that
-  // share a panel run two stages apart rather than one, so a follower's
-  // request comes after the leader's line has arrived rather than while it
-  // is still in flight.
+  // all of its tiles (about 2% less time for the launch at T = 8192).  The
+  // K loop of tile (tt, nt) starts at stage (tt + nt) mod KB, as in
+  // bmm_large_kernel.  (Spacing the tiles that share a panel two stages
+  // apart took the same time but fetched 1.5 GB per launch from beyond L2
+  // instead of 1.0 GB: the 8 tiles sharing a weight tile then spread over 16
+  // stages, longer than its rows stay in the XCD's L2.)
   auto tile_at = [&](int r, int& g, int& t0, int& n0, int& kb0) {
     const int li = (slot + r * 11) % p.wg_per_xcd + r * p.wg_per_xcd;
     const int work = xcd * p.per_xcd + li;
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     g = work / (p.tiles_n * p.tiles_t);
     t0 = tt * kLT;
     n0 = nt * kLN;
-    kb0 = (2 * (tt + nt)) % KB;
+    kb0 = (tt + nt) % KB;
     return true;
   };
 
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // front(cur, first, with_scales): `first` starts the tile's sums;
   // `with_scales` also writes the next tile's staged scales (load_scales) to
   // LDS buffer `scale_sb` before the barrier, so they are visible after it.
-  auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb, bool stores_pending = false) {
+  auto front = [&](const uint8_t* cur, auto first, auto with_scales, int scale_sb) {
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 16>([&](auto K) {
       mfma_k(K, fw[0], fa[0], first);
@@ -681,10 +684,7 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     });
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    if (stores_pending)
-      __builtin_amdgcn_s_waitcnt(kWaitOlder32);          // all but the previous tile's 32 output stores
-    else
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
     if constexpr (decltype(with_scales)::value) {
       store_scales(scale_sb);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm);
@@ -730,9 +730,97 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
 
   const std::true_type yes{};
   const std::false_type no{};
-  bool stores_pending = false;                   // the previous tile stored all 32 of its blocks per wave
+  // ---- epilogue, folded into the next tile's first half-stage
+  //
+  // In the accumulator layout a lane holds one token and two lanes share a
+  // row, so a direct store writes 32 bytes per row.  Instead the wave's
+  // 128 x 128 sub-tile leaves in 8 chunks of 32 rows (accumulator row tile
+  // j) x 64 columns (tiles 2 ip, 2 ip + 1): a chunk is converted to BF16,
+  // written to LDS (the finishing tile's scale buffer, free since the
+  // transition barrier; 4 KiB per wave, 16-byte chunks XOR-swizzled by row),
+  // read back as 8 rows x 128 bytes per instruction and stored.  Right after
+  // a chunk is stored, the two MFMAs that start the next tile's sums in its
+  // blocks are issued, so they run while the next chunk is converted.  The
+  // staging goes through inline asm with its own lgkmcnt waits: written as
+  // plain LDS accesses, the compiler could not tell the run-time scale
+  // buffer from the LDS-DMA targets and waited for all outstanding DMA and
+  // stores before each access.  The restarting MFMAs are inline asm too,
+  // tied to the block's registers: as builtins with a zero accumulator the
+  // register allocator gave the new sums fresh registers and spilled.
+  uint8_t* const stg_base = &lds_sc[0][0][0][0][0][0] + wave * 4096;
+  const int er = lane >> 3, ec = lane & 7;   // staging read side: row in group of 8, 16-byte chunk
+  typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
+  // front_fold(cur, ft0, fn0, fg, fsb): the first half of the next tile's
+  // stage 0 (fragments fw[0] / fa[0], buffer `cur`) with the epilogue of the
+  // finishing tile (ft0, fn0, fg; scale buffer fsb) folded in
+  auto front_fold = [&](const uint8_t* cur, int ft0, int fn0, int fg, int fsb) {
+    uint8_t* const stg = stg_base + fsb * (kScaleWin * kScStep);
+    const uint32_t wa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg));
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<0, 8>([&](auto C) {
+      constexpr int c8 = decltype(C)::value, j = c8 >> 1, ip = c8 & 1;
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        const v16f& v = acc[2 * ip + ii][j];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+          const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+          const int c = ii * 4 + pp * 2 + q2;
+          const uint32_t a = wa + r32 * 128 + ((c ^ (r32 & 7)) << 4);
+          const v4u_t dv = {s0[0], s1[0], s0[1], s1[1]};
+          asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(dv) : "memory");
+        }
+      }
+      v4u_t d0, d1, d2, d3;
+      asm volatile(
+          "s_waitcnt lgkmcnt(0)\n"
+          "ds_read_b128 %0, %4\n"
+          "ds_read_b128 %1, %4 offset:1024\n"
+          "ds_read_b128 %2, %4 offset:2048\n"
+          "ds_read_b128 %3, %4 offset:3072\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+          : "v"(wa + er * 128 + ((ec ^ er) << 4))
+          : "memory");
+      const v4u_t d[4] = {d0, d1, d2, d3};
+#pragma unroll
+      for (int sg = 0; sg < 4; ++sg) {
+        const int t = ft0 + wt * 128 + j * 32 + sg * 8 + er;
+        const int n = fn0 + wn * 128 + ip * 64 + ec * 8;
+        if (t < p.T && n < p.N)
+          *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + fg) * p.N + n) =
+              make_uint4(d[sg][0], d[sg][1], d[sg][2], d[sg][3]);
+      }
+      // the next tile's first MFMAs on this chunk's two blocks (accumulator
+      // input 0, result in the block's own registers)
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                   : "+a"(acc[2 * ip][j])
+                   : "v"(fw[0][2 * ip]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip) & 1), "n"(j & 1),
+                     "n"((2 * ip) >> 1), "n"(j >> 1));
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                   : "+a"(acc[2 * ip + 1][j])
+                   : "v"(fw[0][2 * ip + 1]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip + 1) & 1), "n"(j & 1),
+                     "n"((2 * ip + 1) >> 1), "n"(j >> 1));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<0, 8>([&](auto K) { read_k(K, cur, ch10, ch11, fw[1], fa[1]); });
+    pin_acc();
+    __builtin_amdgcn_sched_barrier(0);
+    // an interior tile issued exactly 32 stores per wave after the DMA of
+    // the next tile's stage 1; vector memory completes in issue order, so the
+    // wait for that DMA can leave the stores in flight
+    if (ft0 + kLT <= p.T && fn0 + kLN <= p.N)
+      __builtin_amdgcn_s_waitcnt(kWaitOlder32);
+    else
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+  };
+
+  front(st0, yes, no, 0);                        // first tile, stage 0 (first half): starts the sums
   for (int r = 0;; ++r) {
-    front(st0, yes, no, 0, stores_pending);      // stage 0 (first half): starts the sums
     int kb = 0;
     for (; kb + 2 < KB; kb += 2) {               // stages kb, kb+1 finish; kb+2 begins
       back(st0, st1, kb + 2, kb + 1, ckb0, csb);
@@ -755,67 +843,8 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     front(st1, no, yes, csb ^ 1);                // waits for it and for the scale loads; stages the scales
     back(st1, st0, 1, 0, nkb0, csb ^ 1);         // next tile's stage 1 -> st1; its stage 0 half 0
 
-    // epilogue of this tile.  In the accumulator layout a lane holds one
-    // token and two lanes share a row, so a direct store writes 32 bytes per
-    // row; instead each 32-row x 64-column piece of the wave's sub-tile goes
-    // through LDS (this tile's scale buffer, free since the transition
-    // barrier; 4 KiB per wave) and leaves as 8 rows x 128 bytes per store.
-    {
-      uint8_t* const stg = &lds_sc[csb][0][0][0][0][0] + wave * 4096;
-      const int lr = lane >> 3, lc = lane & 7;     // read side: row in group of 8, 16-byte chunk
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int ip = 0; ip < 2; ++ip) {
-#pragma unroll
-          for (int ii = 0; ii < 2; ++ii) {
-            const v16f& v = acc[2 * ip + ii][j];
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-              const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
-              const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
-              const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-              const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-              const int c = ii * 4 + pp * 2 + q2;   // 16-byte chunk of the 128-byte row piece
-              const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg)) + r32 * 128 + ((c ^ (r32 & 7)) << 4);
-              typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
-              const v4u_t dv = {s0[0], s1[0], s0[1], s1[1]};
-              asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(dv) : "memory");
-            }
-          }
-          typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
-          v4u_t d0, d1, d2, d3;
-          {
-            const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg)) + lr * 128 + ((lc ^ lr) << 4);
-            // rows lr, 8 + lr, 16 + lr, 24 + lr (row & 7 == lr for all four)
-            asm volatile(
-                "s_waitcnt lgkmcnt(0)\n"
-                "ds_read_b128 %0, %4\n"
-                "ds_read_b128 %1, %4 offset:1024\n"
-                "ds_read_b128 %2, %4 offset:2048\n"
-                "ds_read_b128 %3, %4 offset:3072\n"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
-                : "v"(a)
-                : "memory");
-          }
-          const uint4 d[4] = {make_uint4(d0[0], d0[1], d0[2], d0[3]), make_uint4(d1[0], d1[1], d1[2], d1[3]),
-                              make_uint4(d2[0], d2[1], d2[2], d2[3]), make_uint4(d3[0], d3[1], d3[2], d3[3])};
-#pragma unroll
-          for (int sg = 0; sg < 4; ++sg) {
-            const int t = ct0 + wt * 128 + j * 32 + sg * 8 + lr;
-            const int n = cn0 + wn * 128 + ip * 64 + lc * 8;
-            if (t < p.T && n < p.N)
-              *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + cg) * p.N + n) = d[sg];
-          }
-        }
-      }
-    }
+    front_fold(st0, ct0, cn0, cg, csb);          // next tile's stage 0 (first half) + this tile's epilogue
     if (!more) break;
-    // an interior tile issued exactly 32 stores per wave after the DMA of the
-    // next tile's stage 1; vector memory completes in issue order, so the
-    // next tile's first wait can leave those stores in flight
-    stores_pending = ct0 + kLT <= p.T && cn0 + kLN <= p.N;
     cg = ng;
     ct0 = nt0;
     cn0 = nn0;
