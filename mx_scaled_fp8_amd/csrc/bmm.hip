@@ -755,6 +755,8 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // finishing tile (ft0, fn0, fg; scale buffer fsb) folded in
   auto front_fold = [&](const uint8_t* cur, int ft0, int fn0, int fg, int fsb) {
     uint8_t* const stg = stg_base + fsb * (kScaleWin * kScStep);
+    // LDS byte address for ds_read / ds_write: the low 32 bits of the generic
+    // address (the shared aperture is 4 GiB aligned)
     const uint32_t wa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg));
     __builtin_amdgcn_sched_barrier(0);
     static_for<0, 8>([&](auto C) {
