@@ -150,6 +150,29 @@ def bench_prefill(mx, torch, workloads, steps, warmup, fmt=0):
     return dict(p=p, total_ms=total_ms, wall_s=wall, q_ms=q_ms, b_ms=b_ms, L=L)
 
 
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return None
+
+
+def oracle_wo_a_seconds(x_bits, positions, cos, sin, H, D, G, K, w, w_scale):
+    """Seconds the CPU oracle takes for the quantiser and the GEMM (OCP) on these inputs."""
+    from oracle.formats import OCP as fmt
+    from oracle.gemm import bmm_a8w8_mxscale
+    from oracle.quant import inv_rope_group_quant
+    T = x_bits.shape[0]
+    with np.errstate(invalid="ignore"):
+        t0 = time.perf_counter()
+        rq, rs = inv_rope_group_quant(x_bits, positions, cos, sin, H, D, 64, fmt=fmt)
+        t1 = time.perf_counter()
+        bmm_a8w8_mxscale(rq.reshape(T, G, K), rs.reshape(T, G, -1), w, w_scale, a_fmt=fmt)
+        t2 = time.perf_counter()
+    return t1 - t0, t2 - t1
+
+
 def cpu_baseline(workloads, tokens):
     """The oracle (as it stands) on the first `tokens` tokens of the same chunk."""
     from oracle.gemm import bmm_a8w8_mxscale
@@ -177,7 +200,7 @@ def cpu_baseline(workloads, tokens):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
-def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50):
+def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50, cpu=True):
     """Secondary per-kernel timings: decode batch (cold weights), MXFP8 linear,
     dequantisation, the BF16 arm."""
     dev = torch.device("cuda:0")
@@ -220,6 +243,11 @@ def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50):
                          "bmm_us": us_b, "bmm_us_min": us_b_min, "bmm_GBps": bb / us_b / 1e3,
                          "bmm_hbm_frac": bb / us_b / 1e3 / PEAK_HBM_GBS, "bmm_TFLOPs": p.flops / us_b / 1e6,
                          "weights": "cold (6 rotating copies)"}
+    if cpu:
+        tq, tb = oracle_wo_a_seconds(p.x, p.positions, cos, sin, p.H, p.D, p.G, p.K, p.w, p.w_scale)
+        res["decode_T64"]["cpu_oracle"] = {
+            "quant_s": tq, "bmm_s": tb, "step_us": (tq + tb) * 1e6, "cores": blas_threads(),
+            "note": "the whole decode batch; quantiser single-threaded numpy, fp64 GEMM on BLAS"}
     del ws_copies, x, q, s, out
 
     # MXFP8 linear, M = 64, N = 4096: dequant at load for K % 128 != 0
@@ -245,6 +273,11 @@ def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50):
         lbytes = wbytes + M * K * 2 + M * N * 2
         rec.update(branch="bf16 (dequantised at load)" if K % 128 else "block-scaled fp8", linear_us=us_l,
                    linear_GBps=lbytes / us_l / 1e3, linear_hbm_frac=lbytes / us_l / 1e3 / PEAK_HBM_GBS)
+        if cpu:
+            from oracle.gemm import mx_linear as oracle_linear
+            t0 = time.perf_counter()
+            oracle_linear(xh, wh, wsh)
+            rec["cpu_oracle_us"] = (time.perf_counter() - t0) * 1e6
         lin[f"K{K}"] = rec
     res["mxfp8_linear_M64_N4096"] = lin
     # the pages' production shape: 5120 x 576 shared-expert down_proj at TP4
@@ -443,7 +476,7 @@ def bench_graphs(mx, torch, workloads, calls=40, replays=20):
     return out
 
 
-def bench_long(mx, torch, workloads):
+def bench_long(mx, torch, workloads, cpu=True):
     """The 100,000-token prefill streamed in 8192-token chunks (last 1,696),
     quantiser + GEMM per chunk, OCP then FNUZ activations; activations are
     generated on the GPU (seeded) and resident before timing."""
@@ -478,6 +511,14 @@ def bench_long(mx, torch, workloads):
         ms = a.elapsed_time(b)
         res[name] = {"ms": ms, "tokens_per_s": 1e5 / (ms / 1e3),
                      "TFLOPs": 2 * 100_000 * G * N * K / (ms / 1e3) / 1e12}
+    if cpu:   # the oracle on the last chunk (1,696 tokens), OCP
+        (s0, n), x = chunks[-1], xs[-1]
+        xb = x.cpu().numpy().view(np.uint16)
+        tq, tb = oracle_wo_a_seconds(xb, np.arange(s0, s0 + n, dtype=np.int64), cos, sin, H, D, G, K, w, ws)
+        res["cpu_oracle"] = {"tokens": n, "quant_s": tq, "bmm_s": tb, "tokens_per_s": n / (tq + tb),
+                             "cores": blas_threads(),
+                             "note": "the last chunk of the stream, OCP; quantiser single-threaded numpy, "
+                                     "fp64 GEMM on BLAS"}
     return res
 
 
@@ -560,10 +601,11 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(workloads, args.cpu_tokens)
     if args.extra:
         log("[bench] secondary kernels")
-        rec["kernels"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3)
+        rec["kernels"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3,
+                                      cpu=not args.no_cpu_baseline)
     if args.long:
         log("[bench] 100,000-token chunked prefill")
-        rec["long_prefill_100k"] = bench_long(mx, torch, workloads)
+        rec["long_prefill_100k"] = bench_long(mx, torch, workloads, cpu=not args.no_cpu_baseline)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
