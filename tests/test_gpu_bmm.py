@@ -136,6 +136,31 @@ def test_large_kernel_misaligned_scales():
     assert_gemm_close(host_u16(out), G.bmm_a8w8_mxscale(a, sa, w, sw), "misaligned scales")
 
 
+def test_persistent_matches_large_kernel_bit_exact():
+    # Several tiles per workgroup with ragged T and N, through the persistent
+    # kernel (aligned scales: LDS-staged epilogue folded into the next tile)
+    # and through the one-tile-per-workgroup kernel (the same scales 1 byte
+    # into a larger buffer).  Both sum each block over the same rotated K
+    # order, so the outputs must agree bit for bit; sampled rows are also
+    # checked against the oracle.
+    T, Gn, N, K = 4200, 8, 1008, 2048
+    a, sa, w, sw = workloads.gemm_operands(51, T, Gn, N, K)
+    dev = torch.device("cuda:0")
+    say("bmm persistent vs large", T, Gn, N, K)
+    ad, wd = dev_u8(a), dev_u8(w)
+    o_pers = mx.mx_bmm_a8w8_mxscale(ad, dev_u8(sa), wd, dev_u8(sw))
+    sab = torch.zeros(sa.size + 16, dtype=torch.uint8, device=dev)
+    swb = torch.zeros(sw.size + 16, dtype=torch.uint8, device=dev)
+    sab[1:1 + sa.size] = torch.from_numpy(sa.reshape(-1)).to(dev)
+    swb[1:1 + sw.size] = torch.from_numpy(sw.reshape(-1)).to(dev)
+    o_large = mx.mx_bmm_a8w8_mxscale(ad, sab[1:1 + sa.size].view(sa.shape), wd, swb[1:1 + sw.size].view(sw.shape))
+    torch.cuda.synchronize()
+    op, ol = host_u16(o_pers), host_u16(o_large)
+    assert np.array_equal(op, ol)
+    rows = _sample_rows(T, np.random.default_rng(51))
+    assert_gemm_close(op[rows], G.bmm_a8w8_mxscale(a[rows], sa[rows], w, sw), "persistent vs large")
+
+
 def test_persistent_fnuz_bit_identical():
     T, Gn, N, K = 600, 2, 512, 4096
     a, sa, w, sw = workloads.gemm_operands(31, T, Gn, N, K, a_exp=(-12, -2))
