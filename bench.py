@@ -538,7 +538,7 @@ def main():
                          "scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (the wo_a path is measured on one MI355X); "
+        print("bench.py: the wo_a path runs and is measured on one MI355X only; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
