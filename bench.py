@@ -158,7 +158,7 @@ def blas_threads():
         return None
 
 
-def oracle_wo_a_seconds(x_bits, positions, cos, sin, H, D, G, K, w, w_scale):
+def cpu_baseline_wo_a_seconds(x_bits, positions, cos, sin, H, D, G, K, w, w_scale):
     """Seconds the CPU oracle takes for the quantiser and the GEMM (OCP) on these inputs."""
     from oracle.formats import OCP as fmt
     from oracle.gemm import bmm_a8w8_mxscale
@@ -200,7 +200,37 @@ def cpu_baseline(workloads, tokens):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
-def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50, cpu=True):
+def cpu_baseline_secondary(torch, workloads, kernels, long_rec):
+    """The CPU-baseline leg for the other configs: the oracle timed on the
+    whole decode batch, on the MXFP8 linear at each K and (when the long
+    stream ran) on its last chunk; entries are added to the GPU records."""
+    from oracle.gemm import mx_linear as oracle_linear
+    if kernels is not None:
+        p = workloads.decode_batch()
+        cos, sin = workloads.rope_tables(rows=32768)
+        tq, tb = cpu_baseline_wo_a_seconds(p.x, p.positions, cos, sin, p.H, p.D, p.G, p.K, p.w, p.w_scale)
+        kernels["decode_T64"]["cpu_oracle"] = {
+            "quant_s": tq, "bmm_s": tb, "step_us": (tq + tb) * 1e6, "cores": blas_threads(),
+            "note": "the whole decode batch; quantiser single-threaded numpy, fp64 GEMM on BLAS"}
+        for K, (xh, wh, wsh, _) in workloads.mxfp8_linear().items():
+            t0 = time.perf_counter()
+            oracle_linear(xh, wh, wsh)
+            kernels["mxfp8_linear_M64_N4096"][f"K{K}"]["cpu_oracle_us"] = (time.perf_counter() - t0) * 1e6
+    if long_rec is not None:   # the last chunk of the stream (1,696 tokens), OCP
+        cols, w, ws = workloads.long_prefill_weights()
+        cos, sin = workloads.rope_tables()
+        c = len(workloads.long_prefill_chunks()) - 1
+        s0, n = workloads.long_prefill_chunks()[c]
+        xb = workloads.device_activations(c, n, 65536, cols, torch.device("cuda:0")).cpu().numpy().view(np.uint16)
+        tq, tb = cpu_baseline_wo_a_seconds(xb, np.arange(s0, s0 + n, dtype=np.int64), cos, sin, 128, 512, 16, 4096,
+                                     w, ws)
+        long_rec["cpu_oracle"] = {"tokens": n, "quant_s": tq, "bmm_s": tb, "tokens_per_s": n / (tq + tb),
+                                  "cores": blas_threads(),
+                                  "note": "the last chunk of the stream, OCP; quantiser single-threaded numpy, "
+                                          "fp64 GEMM on BLAS"}
+
+
+def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50):
     """Secondary per-kernel timings: decode batch (cold weights), MXFP8 linear,
     dequantisation, the BF16 arm."""
     dev = torch.device("cuda:0")
@@ -243,11 +273,6 @@ def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50, cpu=True
                          "bmm_us": us_b, "bmm_us_min": us_b_min, "bmm_GBps": bb / us_b / 1e3,
                          "bmm_hbm_frac": bb / us_b / 1e3 / PEAK_HBM_GBS, "bmm_TFLOPs": p.flops / us_b / 1e6,
                          "weights": "cold (6 rotating copies)"}
-    if cpu:
-        tq, tb = oracle_wo_a_seconds(p.x, p.positions, cos, sin, p.H, p.D, p.G, p.K, p.w, p.w_scale)
-        res["decode_T64"]["cpu_oracle"] = {
-            "quant_s": tq, "bmm_s": tb, "step_us": (tq + tb) * 1e6, "cores": blas_threads(),
-            "note": "the whole decode batch; quantiser single-threaded numpy, fp64 GEMM on BLAS"}
     del ws_copies, x, q, s, out
 
     # MXFP8 linear, M = 64, N = 4096: dequant at load for K % 128 != 0
@@ -273,11 +298,6 @@ def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, reps=50, cpu=True
         lbytes = wbytes + M * K * 2 + M * N * 2
         rec.update(branch="bf16 (dequantised at load)" if K % 128 else "block-scaled fp8", linear_us=us_l,
                    linear_GBps=lbytes / us_l / 1e3, linear_hbm_frac=lbytes / us_l / 1e3 / PEAK_HBM_GBS)
-        if cpu:
-            from oracle.gemm import mx_linear as oracle_linear
-            t0 = time.perf_counter()
-            oracle_linear(xh, wh, wsh)
-            rec["cpu_oracle_us"] = (time.perf_counter() - t0) * 1e6
         lin[f"K{K}"] = rec
     res["mxfp8_linear_M64_N4096"] = lin
     # the pages' production shape: 5120 x 576 shared-expert down_proj at TP4
@@ -476,7 +496,7 @@ def bench_graphs(mx, torch, workloads, calls=40, replays=20):
     return out
 
 
-def bench_long(mx, torch, workloads, cpu=True):
+def bench_long(mx, torch, workloads):
     """The 100,000-token prefill streamed in 8192-token chunks (last 1,696),
     quantiser + GEMM per chunk, OCP then FNUZ activations; activations are
     generated on the GPU (seeded) and resident before timing."""
@@ -511,14 +531,6 @@ def bench_long(mx, torch, workloads, cpu=True):
         ms = a.elapsed_time(b)
         res[name] = {"ms": ms, "tokens_per_s": 1e5 / (ms / 1e3),
                      "TFLOPs": 2 * 100_000 * G * N * K / (ms / 1e3) / 1e12}
-    if cpu:   # the oracle on the last chunk (1,696 tokens), OCP
-        (s0, n), x = chunks[-1], xs[-1]
-        xb = x.cpu().numpy().view(np.uint16)
-        tq, tb = oracle_wo_a_seconds(xb, np.arange(s0, s0 + n, dtype=np.int64), cos, sin, H, D, G, K, w, ws)
-        res["cpu_oracle"] = {"tokens": n, "quant_s": tq, "bmm_s": tb, "tokens_per_s": n / (tq + tb),
-                             "cores": blas_threads(),
-                             "note": "the last chunk of the stream, OCP; quantiser single-threaded numpy, "
-                                     "fp64 GEMM on BLAS"}
     return res
 
 
@@ -601,11 +613,13 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(workloads, args.cpu_tokens)
     if args.extra:
         log("[bench] secondary kernels")
-        rec["kernels"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3,
-                                      cpu=not args.no_cpu_baseline)
+        rec["kernels"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3)
     if args.long:
         log("[bench] 100,000-token chunked prefill")
-        rec["long_prefill_100k"] = bench_long(mx, torch, workloads, cpu=not args.no_cpu_baseline)
+        rec["long_prefill_100k"] = bench_long(mx, torch, workloads)
+    if not args.no_cpu_baseline and (args.extra or args.long):
+        log("[bench] CPU oracle on the other configs")
+        cpu_baseline_secondary(torch, workloads, rec.get("kernels"), rec.get("long_prefill_100k"))
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
