@@ -738,9 +738,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // j) x 64 columns (tiles 2 ip, 2 ip + 1): a chunk is converted to BF16,
   // written to LDS (the finishing tile's scale buffer, free since the
   // transition barrier; 4 KiB per wave, 16-byte chunks XOR-swizzled by row),
-  // read back as 8 rows x 128 bytes per instruction and stored.  Right after
-  // a chunk is stored, the two MFMAs that start the next tile's sums in its
-  // blocks are issued, so they run while the next chunk is converted.  The
+  // read back as 8 rows x 128 bytes per instruction and stored.  As soon as
+  // a chunk is in LDS, the two MFMAs that start the next tile's sums in its
+  // blocks are issued, so they run while the chunk makes its LDS round trip
+  // and the next chunk is converted.  The
   // staging goes through inline asm with its own lgkmcnt waits: written as
   // plain LDS accesses, the compiler could not tell the run-time scale
   // buffer from the LDS-DMA targets and waited for all outstanding DMA and
@@ -759,6 +760,9 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     // address (the shared aperture is 4 GiB aligned)
     const uint32_t wa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg));
     __builtin_amdgcn_sched_barrier(0);
+    // the fragments of this half have landed (stated here, the compiler
+    // puts no wait of its own between a chunk's LDS writes and its MFMAs)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm);
     static_for<0, 8>([&](auto C) {
       constexpr int c8 = decltype(C)::value, j = c8 >> 1, ip = c8 & 1;
 #pragma unroll
@@ -776,6 +780,17 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
           asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(dv) : "memory");
         }
       }
+      // the next tile's first MFMAs on this chunk's two blocks (accumulator
+      // input 0, result in the block's own registers; the blocks were read
+      // out above)
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                   : "+a"(acc[2 * ip][j])
+                   : "v"(fw[0][2 * ip]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip) & 1), "n"(j & 1),
+                     "n"((2 * ip) >> 1), "n"(j >> 1));
+      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
+                   : "+a"(acc[2 * ip + 1][j])
+                   : "v"(fw[0][2 * ip + 1]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip + 1) & 1), "n"(j & 1),
+                     "n"((2 * ip + 1) >> 1), "n"(j >> 1));
       v4u_t d0, d1, d2, d3;
       asm volatile(
           "s_waitcnt lgkmcnt(0)\n"
@@ -796,16 +811,6 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
           *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + fg) * p.N + n) =
               make_uint4(d[sg][0], d[sg][1], d[sg][2], d[sg][3]);
       }
-      // the next tile's first MFMAs on this chunk's two blocks (accumulator
-      // input 0, result in the block's own registers)
-      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
-                   : "+a"(acc[2 * ip][j])
-                   : "v"(fw[0][2 * ip]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip) & 1), "n"(j & 1),
-                     "n"((2 * ip) >> 1), "n"(j >> 1));
-      asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel:[%5,%6,0] op_sel_hi:[%7,%8,0]"
-                   : "+a"(acc[2 * ip + 1][j])
-                   : "v"(fw[0][2 * ip + 1]), "v"(fa[0][j]), "v"(swv), "v"(sav), "n"((2 * ip + 1) & 1), "n"(j & 1),
-                     "n"((2 * ip + 1) >> 1), "n"(j >> 1));
       __builtin_amdgcn_sched_barrier(0);
     });
     static_for<0, 8>([&](auto K) { read_k(K, cur, ch10, ch11, fw[1], fa[1]); });
