@@ -759,6 +759,12 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     // LDS byte address for ds_read / ds_write: the low 32 bits of the generic
     // address (the shared aperture is 4 GiB aligned)
     const uint32_t wa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stg));
+    // this lane's store address for rows ft0 + wt*128 + er (+ j*32 + sg*8) and
+    // columns fn0 + wn*128 + ec*8 (+ ip*64): one 64-bit product per tile, the
+    // per-store offsets are compile-time multiples of a uniform row stride
+    const int trow = ft0 + wt * 128 + er, ncol = fn0 + wn * 128 + ec * 8;
+    uint16_t* const obase = p.out + (static_cast<size_t>(trow) * p.G + fg) * p.N + ncol;
+    const size_t rs8 = static_cast<size_t>(8) * p.G * p.N;   // 8 rows
     __builtin_amdgcn_sched_barrier(0);
     // the fragments of this half have landed (stated here, the compiler
     // puts no wait of its own between a chunk's LDS writes and its MFMAs)
@@ -805,10 +811,8 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
       const v4u_t d[4] = {d0, d1, d2, d3};
 #pragma unroll
       for (int sg = 0; sg < 4; ++sg) {
-        const int t = ft0 + wt * 128 + j * 32 + sg * 8 + er;
-        const int n = fn0 + wn * 128 + ip * 64 + ec * 8;
-        if (t < p.T && n < p.N)
-          *reinterpret_cast<uint4*>(p.out + (static_cast<size_t>(t) * p.G + fg) * p.N + n) =
+        if (trow + j * 32 + sg * 8 < p.T && ncol + ip * 64 < p.N)
+          *reinterpret_cast<uint4*>(obase + (j * 4 + sg) * rs8 + ip * 64) =
               make_uint4(d[sg][0], d[sg][1], d[sg][2], d[sg][3]);
       }
       __builtin_amdgcn_sched_barrier(0);
