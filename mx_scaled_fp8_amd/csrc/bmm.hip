@@ -741,13 +741,13 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // read back as 8 rows x 128 bytes per instruction and stored.  As soon as
   // a chunk is in LDS, the two MFMAs that start the next tile's sums in its
   // blocks are issued, so they run while the chunk makes its LDS round trip
-  // and the next chunk is converted.  The
-  // staging goes through inline asm with its own lgkmcnt waits: written as
-  // plain LDS accesses, the compiler could not tell the run-time scale
-  // buffer from the LDS-DMA targets and waited for all outstanding DMA and
-  // stores before each access.  The restarting MFMAs are inline asm too,
-  // tied to the block's registers: as builtins with a zero accumulator the
-  // register allocator gave the new sums fresh registers and spilled.
+  // and the next chunk is converted.  The staging goes through inline asm
+  // with its own lgkmcnt waits: written as plain LDS accesses, the compiler
+  // could not tell the run-time scale buffer from the LDS-DMA targets and
+  // waited for all outstanding DMA and stores before each access.  The
+  // restarting MFMAs are inline asm too, tied to the block's registers: as
+  // builtins with a zero accumulator the register allocator gave the new
+  // sums fresh registers and spilled.
   uint8_t* const stg_base = &lds_sc[0][0][0][0][0][0] + wave * 4096;
   const int er = lane >> 3, ec = lane & 7;   // staging read side: row in group of 8, 16-byte chunk
   typedef unsigned int v4u_t __attribute__((ext_vector_type(4)));
