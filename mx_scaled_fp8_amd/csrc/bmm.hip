@@ -489,13 +489,16 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // bmm_large_kernel.  (Spacing the tiles that share a panel two stages
   // apart took the same time but fetched 1.5 GB per launch from beyond L2
   // instead of 1.0 GB: the 8 tiles sharing a weight tile then spread over 16
-  // stages, longer than its rows stay in the XCD's L2.)
+  // stages, longer than its rows stay in the XCD's L2.)  Token tiles are
+  // taken from the last to the first: the activation rows the quantiser wrote
+  // last are the ones still in the 256 MB last-level cache when the GEMM
+  // starts (about 1.7% less GEMM time right after the quantiser).
   auto tile_at = [&](int r, int& g, int& t0, int& n0, int& kb0) {
     const int li = (slot + r * 11) % p.wg_per_xcd + r * p.wg_per_xcd;
     const int work = xcd * p.per_xcd + li;
     if (li >= p.per_xcd || work >= p.total_tiles) return false;
     const int nt = work % p.tiles_n;
-    const int tt = (work / p.tiles_n) % p.tiles_t;
+    const int tt = p.tiles_t - 1 - (work / p.tiles_n) % p.tiles_t;
     g = work / (p.tiles_n * p.tiles_t);
     t0 = tt * kLT;
     n0 = nt * kLN;
