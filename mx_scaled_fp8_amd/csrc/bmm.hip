@@ -492,14 +492,27 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
   // stages, longer than its rows stay in the XCD's L2.)  Token tiles are
   // taken from the last to the first: the activation rows the quantiser wrote
   // last are the ones still in the 256 MB last-level cache when the GEMM
-  // starts (about 1.7% less GEMM time right after the quantiser).
+  // starts (about 1.7% less GEMM time right after the quantiser).  When
+  // every XCD's range is whole groups, it is walked token tile by token tile
+  // across its groups (n fastest, then group): the rows the quantiser wrote
+  // last are read for all of the XCD's groups first (about 1.4% less).
+  const int tpg = p.tiles_n * p.tiles_t;         // tiles per group
+  const bool by_token = p.per_xcd % tpg == 0 && p.total_tiles == 8 * p.per_xcd;
+  const int gpx = p.per_xcd / tpg;               // groups per XCD when by_token
   auto tile_at = [&](int r, int& g, int& t0, int& n0, int& kb0) {
     const int li = (slot + r * 11) % p.wg_per_xcd + r * p.wg_per_xcd;
     const int work = xcd * p.per_xcd + li;
     if (li >= p.per_xcd || work >= p.total_tiles) return false;
-    const int nt = work % p.tiles_n;
-    const int tt = p.tiles_t - 1 - (work / p.tiles_n) % p.tiles_t;
-    g = work / (p.tiles_n * p.tiles_t);
+    int nt, tt;
+    if (by_token) {
+      nt = li % p.tiles_n;
+      g = xcd * gpx + (li / p.tiles_n) % gpx;
+      tt = p.tiles_t - 1 - li / (p.tiles_n * gpx);
+    } else {
+      nt = work % p.tiles_n;
+      tt = p.tiles_t - 1 - (work / p.tiles_n) % p.tiles_t;
+      g = work / tpg;
+    }
     t0 = tt * kLT;
     n0 = nt * kLN;
     kb0 = (tt + nt) % KB;
