@@ -88,8 +88,12 @@ def test_decode_kernel_fnuz():
 # K = 2048 and 4096 (16 or 32 K-stages) take the persistent kernel: tile counts
 # below one per XCD, one per workgroup, and several per workgroup (T = 4200:
 # 340 tiles on 256 workgroups), with ragged T and N tiles.  Large cases are
-# checked on sampled rows (first, last, tile edges and random ones).
-PERSIST_SHAPES = [(300, 1, 272, 2048), (1000, 3, 512, 4096), (4200, 5, 1024, 2048), (2600, 2, 784, 4096)]
+# checked on sampled rows (first, last, tile edges and random ones).  The
+# last two split the tiles into whole groups per XCD, which the kernel walks
+# token tile by token tile across the XCD's groups (3 groups per XCD, one
+# tile per workgroup; 2 groups per XCD, two rounds).
+PERSIST_SHAPES = [(300, 1, 272, 2048), (1000, 3, 512, 4096), (4200, 5, 1024, 2048), (2600, 2, 784, 4096),
+                  (512, 24, 256, 2048), (4096, 16, 512, 2048)]
 
 
 def _sample_rows(T, rng, n=48):
