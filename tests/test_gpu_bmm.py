@@ -254,3 +254,27 @@ def test_prefill_chunk_sampled_rows():
     rq, rs = inv_rope_group_quant(p.x[rows], p.positions[rows], cos, sin, p.H, p.D, 64)
     ref = G.bmm_a8w8_mxscale(rq.reshape(len(rows), p.G, p.K), rs.reshape(len(rows), p.G, -1), p.w, p.w_scale)
     assert_gemm_close(out, ref, "prefill")
+
+
+@pytest.mark.slow
+def test_five_chunks_in_one_call():
+    """T = 40960 (five prefill chunks) in one launch: the activations span
+    2.7 GB, so rows from t = 32768 on start past byte 2^31.  Seeded random
+    FP8 codes (no NaN code) and scale bytes, drawn on the device; sampled rows
+    on both sides of that boundary are checked against the oracle."""
+    T, Gn, N, K = 40960, 16, 1024, 4096
+    say("bmm one call T=40960 G=16 N=1024 K=4096")
+    _, _, w, sw = workloads.gemm_operands(515, 1, Gn, N, K)
+    gen = torch.Generator(device="cuda").manual_seed(515)
+    a = torch.randint(0, 256, (T, Gn, K), dtype=torch.uint8, device="cuda", generator=gen)
+    a[(a & 0x7F) == 0x7F] = 0x7E
+    sa = torch.randint(115, 126, (T, Gn, K // 128), dtype=torch.uint8, device="cuda", generator=gen)
+    out = mx.mx_bmm_a8w8_mxscale(a, sa, dev_u8(w), dev_u8(sw))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 8191, 8192, 32767, 32768, 32769, T - 256, T - 1],
+                                     np.random.default_rng(515).integers(0, T, 16)]))
+    idx = torch.from_numpy(rows).cuda()
+    got = host_u16(out[idx].contiguous())
+    ra, rsa = a[idx].cpu().numpy(), sa[idx].cpu().numpy()
+    del a, sa, out
+    assert_gemm_close(got, G.bmm_a8w8_mxscale(ra, rsa, w, sw), "T=40960 one call")
