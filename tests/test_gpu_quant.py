@@ -163,3 +163,30 @@ def test_prefill_chunk_sampled_rows(tables):
     rq, rs = inv_rope_group_quant(p.x[rows], p.positions[rows], cos, sin, p.H, p.D, 64)
     n = assert_codes_close(q[rows], rq, s[rows], rs, F.OCP, exact=False, what="prefill")
     assert n == 0
+
+
+@pytest.mark.slow
+def test_call_split_into_two_launches(tables):
+    """H*D = 65536 and T = 262,243 tokens: 2^31 or more 8-element chunks, so the
+    call runs as two launches (262,143 rows, then 100).  34 GB of seeded random
+    BF16 with |x| < 2 (no Inf or NaN), drawn on the device, and random
+    positions; sampled rows on both sides of the split are checked against the
+    oracle."""
+    H, D, T = 128, 512, 262243
+    cos, sin, dcos, dsin = tables
+    say("quant one call T=262243 H=128 D=512 (two launches)")
+    gen = torch.Generator(device="cuda").manual_seed(616)
+    x = torch.randint(-32768, 32768, (T, H * D), dtype=torch.int16, device="cuda", generator=gen)
+    x.bitwise_and_(~0x4000)
+    pos = torch.randint(0, cos.shape[0], (T,), dtype=torch.int64, device="cuda", generator=gen)
+    q, s = mx.mx_inv_rope_group_quant(x, pos, dcos, dsin, H, D, 64)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 262142, 262143, 262144, T - 1],
+                                     np.random.default_rng(616).integers(0, T, 8)]))
+    idx = torch.from_numpy(rows).cuda()
+    xr, pr = host_u16(x[idx].contiguous()), pos[idx].cpu().numpy()
+    qr, sr = host_u8(q[idx].contiguous()), host_u8(s[idx].contiguous())
+    del x, q, s
+    rq, rs = inv_rope_group_quant(xr, pr, cos, sin, H, D, 64)
+    n = assert_codes_close(qr, rq, sr, rs, F.OCP, exact=False, what="two launches")
+    assert n == 0
