@@ -114,6 +114,49 @@ def _dev(t, name, itemsize=None):
     return t.data_ptr()
 
 
+def _shape(t, shape, name):
+    """Checks the exact shape of a tensor the sizes passed to the library are
+    read from (before any pointer is taken: a wrong shape must not reach the
+    C ABI, which takes raw pointers and cannot check it)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _numel(t, n, name):
+    """Checks the element count of a tensor whose layout is fixed by the call
+    (scales, outputs): any shape with exactly n elements is accepted."""
+    if t is None:
+        return
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n} (shape {tuple(t.shape)})")
+
+
+def _same_device(ref, *ts):
+    for name, t in ts:
+        if t is not None and isinstance(t, torch.Tensor) and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _rope_args(x, positions, cos, sin, T, rope_dim):
+    """Shape and dtype checks of the rotation inputs; returns max_pos."""
+    if rope_dim < 0 or rope_dim % 2:
+        raise ValueError(f"rope_dim = {rope_dim} must be even and >= 0")
+    if rope_dim == 0 or T == 0:
+        return cos.shape[0] if cos is not None else 0
+    if positions is None or cos is None or sin is None:
+        raise ValueError("rope_dim > 0 needs positions, cos and sin")
+    if positions.dtype != torch.int64:
+        raise ValueError(f"positions must be int64 (got {positions.dtype})")
+    _numel(positions, T, "positions")
+    if cos.dim() != 2 or cos.shape[1] != rope_dim // 2:
+        raise ValueError(f"cos has shape {tuple(cos.shape)}, expected [max_pos, {rope_dim // 2}]")
+    _shape(sin, cos.shape, "sin")
+    _same_device(x, ("positions", positions), ("cos", cos), ("sin", sin))
+    return cos.shape[0]
+
+
 def _stream(t):
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -153,12 +196,20 @@ def mx_reset_counters():
 def mx_inv_rope_group_quant(x, positions, cos, sin, H, D, rope_dim, rope_style=MX_ROPE_INTERLEAVED,
                             group=128, fmt=MX_FP8_E4M3_OCP, q=None, scale=None):
     """x BF16 [T, H*D] -> (q uint8 [T, H*D], scale uint8 [T, H*D/group])."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H*D] (got shape {tuple(x.shape)})")
     T = x.shape[0]
+    _shape(x, (T, H * D), "x")
+    if group <= 0 or (H * D) % group:
+        raise ValueError(f"H*D = {H * D} is not a multiple of the group {group}")
+    max_pos = _rope_args(x, positions, cos, sin, T, rope_dim)
+    _numel(q, T * H * D, "q")
+    _numel(scale, T * (H * D) // group, "scale")
+    _same_device(x, ("q", q), ("scale", scale))
     if q is None:
         q = torch.empty((T, H * D), dtype=torch.uint8, device=x.device)
     if scale is None:
         scale = torch.empty((T, (H * D) // group), dtype=torch.uint8, device=x.device)
-    max_pos = cos.shape[0] if cos is not None else 0
     _check(lib().mx_inv_rope_group_quant(
         _dev(x, "x", 2), _dev(positions, "positions", 8) if positions is not None else None,
         _dev(cos, "cos", 2) if cos is not None else None, _dev(sin, "sin", 2) if sin is not None else None,
@@ -169,8 +220,15 @@ def mx_inv_rope_group_quant(x, positions, cos, sin, H, D, rope_dim, rope_style=M
 
 def mx_bmm_a8w8_mxscale(a, a_scale, w, w_scale, a_fmt=MX_FP8_E4M3_OCP, out=None):
     """a uint8 [T,G,K], a_scale [T,G,K/128], w uint8 [G,N,K], w_scale [G,N,K/128] -> BF16 [T,G,N]."""
+    if a.dim() != 3 or w.dim() != 3:
+        raise ValueError(f"a must be [T,G,K] and w [G,N,K] (got {tuple(a.shape)} and {tuple(w.shape)})")
     T, G, K = a.shape
     N = w.shape[1]
+    _shape(w, (G, N, K), "w")
+    _numel(a_scale, T * G * (K // 128), "a_scale")
+    _numel(w_scale, G * N * (K // 128), "w_scale")
+    _numel(out, T * G * N, "out")
+    _same_device(a, ("a_scale", a_scale), ("w", w), ("w_scale", w_scale), ("out", out))
     if out is None:
         out = torch.empty((T, G, N), dtype=torch.bfloat16, device=a.device)
     _check(lib().mx_bmm_a8w8_mxscale(_dev(a, "a", 1), _dev(a_scale, "a_scale", 1), a_fmt, _dev(w, "w", 1),
@@ -184,6 +242,11 @@ def mx_woa_expand_scales(scale, G, N, K, block_n=1, out=None):
     kind = MX_SCALE_F32 if scale.dtype == torch.float32 else MX_SCALE_E8M0
     if kind == MX_SCALE_E8M0 and scale.element_size() != 1:
         raise ValueError("scale must be uint8 (E8M0) or float32")
+    if block_n not in (1, 128) or G < 1 or N < 1 or K < 128 or K % 128:
+        raise ValueError(f"block_n = {block_n}, G = {G}, N = {N}, K = {K} not accepted")
+    _numel(scale, G * (-(-N // block_n)) * (K // 128), "scale")
+    _numel(out, G * N * (K // 128), "out")
+    _same_device(scale, ("out", out))
     if out is None:
         out = torch.empty((G, N, K // 128), dtype=torch.uint8, device=scale.device)
     rejects = torch.zeros(1, dtype=torch.int32, device=scale.device)
@@ -196,10 +259,15 @@ def mx_woa_expand_scales(scale, G, N, K, block_n=1, out=None):
 
 def mx_inv_rope_bf16(x, positions, cos, sin, H, D, rope_dim, rope_style=MX_ROPE_INTERLEAVED, out=None):
     """x BF16 [T, H*D] -> rotated BF16 [T, H*D]; ``out=x`` rotates in place."""
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H*D] (got shape {tuple(x.shape)})")
     T = x.shape[0]
+    _shape(x, (T, H * D), "x")
+    max_pos = _rope_args(x, positions, cos, sin, T, rope_dim)
+    _numel(out, T * H * D, "out")
+    _same_device(x, ("out", out))
     if out is None:
         out = torch.empty((T, H * D), dtype=x.dtype, device=x.device)
-    max_pos = cos.shape[0] if cos is not None else 0
     _check(lib().mx_inv_rope_bf16(
         _dev(x, "x", 2), _dev(positions, "positions", 8) if positions is not None else None,
         _dev(cos, "cos", 2) if cos is not None else None, _dev(sin, "sin", 2) if sin is not None else None,
@@ -209,8 +277,13 @@ def mx_inv_rope_bf16(x, positions, cos, sin, H, D, rope_dim, rope_style=MX_ROPE_
 
 def mx_bmm_bf16(x, w, out=None):
     """x BF16 [T,G,K], w BF16 [G,N,K] -> BF16 [T,G,N]."""
+    if x.dim() != 3 or w.dim() != 3:
+        raise ValueError(f"x must be [T,G,K] and w [G,N,K] (got {tuple(x.shape)} and {tuple(w.shape)})")
     T, G, K = x.shape
     N = w.shape[1]
+    _shape(w, (G, N, K), "w")
+    _numel(out, T * G * N, "out")
+    _same_device(x, ("w", w), ("out", out))
     if out is None:
         out = torch.empty((T, G, N), dtype=torch.bfloat16, device=x.device)
     _check(lib().mx_bmm_bf16(_dev(x, "x", 2), _dev(w, "w", 2), _dev(out, "out", 2), T, G, N, K, _stream(x)))
@@ -221,7 +294,14 @@ def mx_bmm_bf16(x, w, out=None):
 
 def mx_dequant_mxfp8_to_bf16(w, w_scale, block=MX_LINEAR_BLOCK, out=None):
     """w uint8 OCP [N,K], w_scale [N,K/block] -> BF16 [N,K]."""
+    if w.dim() != 2:
+        raise ValueError(f"w must be [N, K] (got shape {tuple(w.shape)})")
     N, K = w.shape
+    if block not in (32, 128) or K % block:
+        raise ValueError(f"K = {K} is not a multiple of the block {block} (32 or 128)")
+    _numel(w_scale, N * (K // block), "w_scale")
+    _numel(out, N * K, "out")
+    _same_device(w, ("w_scale", w_scale), ("out", out))
     if out is None:
         out = torch.empty((N, K), dtype=torch.bfloat16, device=w.device)
     _check(lib().mx_dequant_mxfp8_to_bf16(_dev(w, "w", 1), _dev(w_scale, "w_scale", 1), _dev(out, "out", 2),
@@ -239,9 +319,20 @@ def mx_linear_workspace_bytes(M, N, K, w_elem_bytes):
 
 def mx_linear(x, w, w_scale=None, out=None, workspace=None):
     """x BF16 [M,K] @ W^T; W is FP8 uint8 [N,K] (+ w_scale [N,K/32]) or BF16 [N,K]."""
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"x must be [M,K] and w [N,K] (got {tuple(x.shape)} and {tuple(w.shape)})")
     M, K = x.shape
     N = w.shape[0]
     eb = w.element_size()
+    _shape(w, (N, K), "w")
+    if eb == 1:
+        if w_scale is None:
+            raise ValueError("an FP8 weight needs w_scale [N, K/32]")
+        if K % MX_LINEAR_BLOCK:
+            raise ValueError(f"K = {K} is not a multiple of {MX_LINEAR_BLOCK}")
+        _numel(w_scale, N * (K // MX_LINEAR_BLOCK), "w_scale")
+    _numel(out, M * N, "out")
+    _same_device(x, ("w", w), ("w_scale", w_scale), ("out", out), ("workspace", workspace))
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     need = mx_linear_workspace_bytes(M, N, K, eb)
@@ -269,6 +360,10 @@ def mx_f32_pow2_to_e8m0(x):
 def mx_f32_pow2_to_e8m0_device(x, out=None, reject_count=None):
     """Device: float32 tensor -> E8M0 uint8 tensor; rejected values become 0xFF
     and are counted into `reject_count` (int32 GPU tensor of one element) if given."""
+    _numel(out, x.numel(), "out")
+    if reject_count is not None and reject_count.numel() < 1:
+        raise ValueError("reject_count must hold one int32")
+    _same_device(x, ("out", out), ("reject_count", reject_count))
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(lib().mx_f32_pow2_to_e8m0_device(_dev(x, "x", 4), _dev(out, "out", 1), x.numel(),
@@ -292,6 +387,8 @@ def mx_f32_to_e4m3_fnuz(x):
 
 
 def mx_f32_to_e4m3_device(x, fmt=MX_FP8_E4M3_OCP, out=None):
+    _numel(out, x.numel(), "out")
+    _same_device(x, ("out", out))
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(lib().mx_f32_to_e4m3_device(_dev(x, "x", 4), _dev(out, "out", 1), x.numel(), fmt, _stream(x)))

@@ -311,10 +311,14 @@ mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const ui
   MX_CHECK(K % MX_LINEAR_BLOCK == 0, "%s: K = %lld is not a multiple of %d", fn, (long long)K, MX_LINEAR_BLOCK);
   MX_CHECK(N % 16 == 0, "%s: N = %lld is not a multiple of 16", fn, (long long)N);
   MX_CHECK(w_elem_bytes == 1 || w_elem_bytes == 2, "%s: w_elem_bytes = %d (1 = FP8, 2 = BF16)", fn, w_elem_bytes);
-  MX_CHECK(M <= (int64_t(1) << 30) && N * K < (int64_t(1) << 40), "%s: shape too large", fn);
+  // the kernels index K, M*K and N*K with 32-bit and 40-bit offsets
+  MX_CHECK(M <= (int64_t(1) << 30) && K < (int64_t(1) << 31) && N * K < (int64_t(1) << 40) &&
+               M * K < (int64_t(1) << 40),
+           "%s: shape too large (M = %lld, N = %lld, K = %lld)", fn, (long long)M, (long long)N, (long long)K);
   const bool fp8 = w_elem_bytes == 1;
   const bool aligned_k = K % MX_LINEAR_K_ALIGN == 0;
-  if (fp8 && aligned_k) MX_CHECK(M <= 64, "%s: the block-scaled path takes M <= 64 rows (M = %lld)", fn, (long long)M);
+  if (fp8 && aligned_k && M > 64)
+    return fail(MX_ERR_UNSUPPORTED, "%s: the block-scaled path takes M <= 64 rows (M = %lld)", fn, (long long)M);
   const size_t need = mx_linear_workspace_bytes(M, N, K, w_elem_bytes);
   if (M == 0 || N == 0) { clear_error(); return MX_OK; }
   MX_CHECK(x && w && out, "%s: null tensor pointer", fn);

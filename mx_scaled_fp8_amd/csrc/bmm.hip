@@ -42,8 +42,9 @@
 //    K-steps; the waves split n.  A BF16 mode serves the BF16 arm.
 //  * bmm_small_kernel (T <= 64, other K): the 4 waves split K, operands
 //    double-buffered in registers, partial sums reduced through LDS.
-//  * gemm_mx32_dma_kernel / gemm_mx32_dma1_kernel: the MXFP8 linear's
-//    block-32 GEMM (M <= 64 / M <= 16) on the decode kernel's ring.
+//  * gemm_mx32_dma_kernel: the MXFP8 linear's block-32 GEMM (M <= 64) on the
+//    decode kernel's ring, for the shapes the weight-resident kernels of
+//    linear_mx32.hip do not take.
 #include <algorithm>
 #include <type_traits>
 
@@ -1363,106 +1364,6 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
   if (t < p.T && n < p.N) *reinterpret_cast<uint2*>(p.out + static_cast<size_t>(t) * p.N + n) = pack4_bf16(acc);
 }
 
-// The same ring for up to 16 rows (a decode batch of the linear): a stage is
-// 16 W rows and 16 x rows (4 KiB), one DMA instruction per wave; stage kt is
-// kept by wave kt % 4, and the four partial sums meet in LDS.
-constexpr int kLin1Rows = 32;
-constexpr int kLin1Stage = kLin1Rows * kBK;        // 4 KiB
-constexpr int kLin1ScaleMax = kLin1Rows * 256;     // scale rows of K <= 8192
-
-__global__ __launch_bounds__(256, 1) void gemm_mx32_dma1_kernel(SmallArgs p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t s0[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s1[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s3[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s4[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s5[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s6[kLin1Stage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s7[kLin1Stage];
-  __shared__ __attribute__((aligned(16))) uint8_t scl[kLin1ScaleMax];  // [16 W rows | 16 x rows][K/32]
-  __shared__ float red[4][4][64];
-  uint8_t* const ring[kLinR] = {s0, s1, s2, s3, s4, s5, s6, s7};
-
-  const int n0 = blockIdx.x * kLinRowsW;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int KB = p.K / kBK;
-  const int SPK = 4 * KB;                             // scale bytes per row (block 32)
-
-  // ---- scale rows by LDS-DMA, before the operand stages
-  const int sc_bytes = kLin1Rows * SPK;
-  for (int ii = wave; ii * 256 < sc_bytes; ii += 4) {
-    const int byte = ii * 256 + 4 * lane;
-    if (byte < sc_bytes) {
-      const int r = byte / SPK, off = byte - r * SPK;
-      const uint8_t* src = r < kLinRowsW ? p.sw + static_cast<size_t>(min(n0 + r, p.N - 1)) * SPK + off
-                                         : p.sa + static_cast<size_t>(min(r - kLinRowsW, p.T - 1)) * SPK + off;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(scl + ii * 256), 4, 0, 0);
-    }
-  }
-
-  // ---- operand DMA: wave w moves stage rows 8w..8w+7 (W rows 0..15, then x rows 0..15)
-  const int r = 8 * wave + (lane >> 3);
-  const uint32_t chunk = static_cast<uint32_t>((lane & 7) ^ swz8(r)) * 16;
-  const uint8_t* src_row = r < kLinRowsW ? p.w + static_cast<size_t>(min(n0 + r, p.N - 1)) * p.K + chunk
-                                         : p.a + static_cast<size_t>(min(r - kLinRowsW, p.T - 1)) * p.K + chunk;
-  auto issue = [&](uint8_t* slot, int kt) {
-    const size_t ko = static_cast<size_t>(min(kt, KB - 1)) * kBK;   // past the end: a harmless refetch
-    __builtin_amdgcn_global_load_lds(src_row + ko, (lds_void_t*)(slot + 8 * wave * kBK), 16, 0, 0);
-  };
-#pragma unroll
-  for (int u = 0; u < kLinR - 1; ++u) issue(ring[u], u);
-
-  const int sw16 = swz8(lane & 15);
-  const int q = lane >> 4;
-  const int c0 = (q ^ sw16) * 16, c1 = ((q + 4) ^ sw16) * 16;
-  const int rdW = (lane & 15) * kBK;
-  const int rdA = (kLinRowsW + (lane & 15)) * kBK;
-  const uint8_t* sclW = scl + (lane & 15) * SPK + q;
-  const uint8_t* sclA = scl + (kLinRowsW + (lane & 15)) * SPK + q;
-  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  constexpr int kWaitStage = 0x0076;                 // vmcnt(6) lgkmcnt(0): 1 instruction x (kLinR - 2) stages
-  static_assert(kLinR - 2 == 6, "wait count");
-
-#pragma unroll 1
-  for (int kt0 = 0; kt0 < KB; kt0 += kLinR) {
-#pragma unroll
-    for (int u = 0; u < kLinR; ++u) {
-      const int kt = kt0 + u;
-      if (kt >= KB) break;                          // uniform: every wave leaves at the same stage
-      __builtin_amdgcn_s_waitcnt(kWaitStage);
-      __builtin_amdgcn_s_barrier();
-      issue(ring[(u + kLinR - 1) % kLinR], kt + kLinR - 1);
-      // every wave multiplies the stage and wave kt % 4 keeps the product (kt0
-      // is a multiple of 4): a select, not a branch, so that the compiler
-      // keeps track of the DMA around it
-      const uint8_t* st = ring[u];
-      const v8i fw = make_v8i(*reinterpret_cast<const uint4*>(st + rdW + c0),
-                              *reinterpret_cast<const uint4*>(st + rdW + c1));
-      const v8i fa = make_v8i(*reinterpret_cast<const uint4*>(st + rdA + c0),
-                              *reinterpret_cast<const uint4*>(st + rdA + c1));
-      const v4f prod = mfma_scaled(fw, fa, acc, sclW[4 * kt], sclA[4 * kt]);
-      const bool mine = wave == (u & 3);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = mine ? prod[e] : acc[e];
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
-
-#pragma unroll
-  for (int e = 0; e < 4; ++e) red[wave][e][lane] = acc[e];
-  __syncthreads();
-  if (wave == 0) {
-    v4f sum;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sum[e] = red[0][e][lane] + red[1][e][lane] + red[2][e][lane] + red[3][e][lane];
-    const int t = lane & 15;
-    const int n = n0 + 4 * q;
-    if (t < p.T && n < p.N) *reinterpret_cast<uint2*>(p.out + static_cast<size_t>(t) * p.N + n) = pack4_bf16(sum);
-  }
-}
-
 // LDS the small-T kernel stages its scale rows in (dynamic shared memory).
 constexpr size_t kSmallScaleLdsMax = 48 * 1024;
 template <int NT, int SB>
@@ -1547,13 +1448,8 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
-  if (M <= 16 && K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
-    SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
-                static_cast<int>(K), static_cast<int>((N + kLinRowsW - 1) / kLinRowsW)};
-    gemm_mx32_dma1_kernel<<<s.n_groups, 256, 0, stream>>>(s);
-    return launch_status("mx_linear (block-scaled FP8 GEMM)");
-  }
-  // the LDS-DMA ring for 17 to 64 rows (M = 64, N = 4096: 10.9 -> 7.8 us at K = 1152)
+  // the LDS-DMA ring (M = 64, N = 4096: 10.9 -> 7.8 us at K = 1152 against
+  // bmm_small_kernel<1, 32>)
   if (K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
     SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
                 static_cast<int>(K), static_cast<int>((N + kLinRowsW - 1) / kLinRowsW)};

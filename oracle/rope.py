@@ -17,9 +17,15 @@ not spell the rotation out, so the readings taken here are:
   Functional fixes ..." (Purpose) shows the unfused reference materialising
   BF16 here.
 
-Pins: position 0 is the identity; a hand-computed rotation at position 1; the
-conjugate-multiplication form in fp64 complex arithmetic; forward after
-inverse returns the input within the table's precision (tests/test_oracle_rope.py).
+Pins (tests/test_oracle_rope.py): position 0 is the identity; a hand-computed
+rotation at position 1; the conjugate-multiplication form in fp64 complex
+arithmetic; forward after inverse returns the input within the table's
+precision; the split-half pairing is the interleaved one up to a permutation
+of the rotated dims; and inputs derived in exact rationals
+(tests/golden/rope_rounding_cases.txt) whose BF16 result is fixed by the fp32
+rounding of the sum -- an fp64 rotation rounded once gives other bits there.
+Products of two BF16 values are exact in fp32, so whether the products are
+rounded on their own or fused into the sum cannot change any result.
 """
 
 import numpy as np

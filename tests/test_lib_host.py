@@ -188,7 +188,10 @@ def test_linear_validation(dry):
     assert f(N=100) == mx.MX_ERR_INVALID_ARG
     assert f(eb=4) == mx.MX_ERR_INVALID_ARG
     assert f(s=None) == mx.MX_ERR_INVALID_ARG
-    assert f(K=1152, M=65) == mx.MX_ERR_INVALID_ARG
+    assert f(K=1152, M=65) == mx.MX_ERR_UNSUPPORTED                # the caller's cue to fall back
+    # K on its own past 2^31 (N small enough for N*K): rejected before any
+    # kernel narrows it to 32 bits
+    assert f(K=1 << 31, N=16, M=1, eb=2, ws=None, wsb=0) == mx.MX_ERR_INVALID_ARG
 
 
 def _rope_bf16(**kw):

@@ -185,3 +185,17 @@ def test_f32_pow2_to_e8m0_every_power():
     assert np.array_equal(b.astype(int), n + 127)
     # decode(encode(s)) == s
     assert np.array_equal(F.e8m0_decode(b), x.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt,tdtype", [(F.OCP, torch.float8_e4m3fn), (F.FNUZ, torch.float8_e4m3fnuz)])
+def test_e4m3_decode_table_matches_torch_cast(fmt, tdtype):
+    """The decode table against a library routine: torch's float8 -> float32
+    CPU cast of every one of the 256 codes (NaN codes compared as NaN)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(tdtype).to(torch.float32).numpy().astype(np.float64)
+    ours = F.e4m3_decode(np.arange(256, dtype=np.uint8), fmt)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zeros agree too
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))

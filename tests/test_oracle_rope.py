@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import workloads
+from conftest import read_golden
 from oracle import formats as F
 from oracle.rope import inverse_rope, pair_indices, INTERLEAVED, NEOX
 
@@ -102,3 +103,82 @@ def test_forward_after_inverse_is_identity(style):
 def test_rope_dim_zero_is_identity():
     x = _rand_x(4, 2, 128, 6)
     assert np.array_equal(inverse_rope(x, np.arange(4), COS, SIN, 2, 128, 0), x)
+
+
+# --------------------------------------------------------------- fp32 rounding
+#
+# tests/golden/rope_rounding_cases.txt holds inputs whose BF16 result depends on
+# the fp32 rounding of the rotation's sum (derived in exact rationals by
+# tests/golden/make_rope_rounding_cases.py).  Products of BF16 values are exact
+# in fp32, so a fused multiply-add cannot differ from separately rounded
+# products; what these cases fix is that the sum is rounded to fp32 before the
+# BF16 rounding, not rotated in fp64 and rounded once.
+
+ROUNDING = read_golden("rope_rounding_cases.txt")
+
+
+def _case_input(row, D, R, style):
+    pos, i = int(row[0]), int(row[1])
+    xb, yb = int(row[4], 16), int(row[5], 16)
+    i0, i1 = pair_indices(D, R, style)
+    x = np.zeros((1, D), np.uint16)
+    x[0, i0[i]], x[0, i1[i]] = xb, yb
+    return x, np.array([pos], np.int64), i0[i], i1[i]
+
+
+@pytest.mark.parametrize("style", [INTERLEAVED, NEOX])
+@pytest.mark.parametrize("row", ROUNDING, ids=lambda r: f"pos{r[0]}-i{r[1]}-{r[10][0]}")
+def test_fp32_sum_rounding_golden(row, style):
+    pos, i = int(row[0]), int(row[1])
+    assert (COS[pos, i], SIN[pos, i]) == (int(row[2], 16), int(row[3], 16))
+    D = R = 64
+    x, p, a, b = _case_input(row, D, R, style)
+    out = inverse_rope(x, p, COS, SIN, 1, D, R, style)
+    assert (out[0, a], out[0, b]) == (int(row[6], 16), int(row[7], 16))
+
+
+@pytest.mark.parametrize("row", ROUNDING, ids=lambda r: f"pos{r[0]}-i{r[1]}-{r[10][0]}")
+def test_fp64_rotation_fails_the_rounding_pin(row):
+    """A rotation in fp64 rounded once to BF16 -- the plausible mistake the
+    golden cases are there to catch -- gives a different BF16 result."""
+    pos, i = int(row[0]), int(row[1])
+    c = float(F.bf16_to_f64(COS[pos, i]))
+    s = float(F.bf16_to_f64(SIN[pos, i]))
+    x = float(F.bf16_to_f64(np.uint16(int(row[4], 16))))
+    y = float(F.bf16_to_f64(np.uint16(int(row[5], 16))))
+    # exact in fp64: 16-bit products, sums within 53 bits
+    mx = F.f64_to_bf16_rne(np.array([x * c + y * s, y * c - x * s]))
+    assert (int(mx[0]), int(mx[1])) == (int(row[8], 16), int(row[9], 16))
+    assert (int(mx[0]), int(mx[1])) != (int(row[6], 16), int(row[7], 16))
+
+
+def test_products_of_bf16_are_exact_in_fp32():
+    """Why no FMA variant can differ: a product of two BF16 values has at most
+    16 significant bits, so fp32 holds it exactly (checked on every pair of
+    positive mantissas; the exponent only shifts the product)."""
+    m = np.arange(128, 256, dtype=np.int64)
+    prod = m[:, None] * m[None, :]                 # < 2^16
+    assert prod.max() < 2 ** 16
+    a = (m.astype(np.float32) / 128)[:, None] * (m.astype(np.float32) / 128)[None, :]
+    assert np.array_equal(a.astype(np.float64) * 2 ** 14, prod.astype(np.float64))
+
+
+@pytest.mark.parametrize("R", [16, 64, 128])
+def test_interleaved_is_neox_up_to_a_permutation(R):
+    """Moving interleaved pair i, dims (2i, 2i+1) of the rotated slice, to the
+    split-half dims (i, i + R/2) and rotating with the split-half pairing gives
+    the interleaved rotation, moved the same way."""
+    T, H, D = 16, 3, 128
+    x = _rand_x(T, H, D, 7)
+    pos = np.random.default_rng(8).integers(0, 4096, T)
+    base, half = D - R, R // 2
+    perm = np.arange(D)                     # neox dim j takes interleaved dim perm[j]
+    perm[base:base + half] = base + 2 * np.arange(half)
+    perm[base + half:] = base + 2 * np.arange(half) + 1
+    xv = x.reshape(T, H, D)
+    xn = np.ascontiguousarray(xv[:, :, perm]).reshape(T, H * D)
+    cos, sin = workloads.rope_tables(rows=4096, rope_dim=R)
+    ri = inverse_rope(x, pos, cos, sin, H, D, R, INTERLEAVED).reshape(T, H, D)
+    rn = inverse_rope(xn, pos, cos, sin, H, D, R, NEOX).reshape(T, H, D)
+    assert np.array_equal(rn, ri[:, :, perm])
+    assert not np.array_equal(ri, xv)       # the rotation did something
