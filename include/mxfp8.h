@@ -17,7 +17,8 @@
  *  - Tensor arguments are raw pointers.  "device" pointers must point to GPU
  *    memory of the current HIP device; "host" pointers to CPU memory.  The
  *    caller owns all memory (inputs, outputs, workspaces); the library
- *    allocates no device memory and keeps no tensor state.
+ *    allocates no device memory and keeps no tensor state (the one exception,
+ *    mx_linear_noalloc's fixed scratch array, is part of the loaded code).
  *  - Layouts are dense, row-major, last index contiguous, exactly as written
  *    in each comment ([T, G, K] means element (t,g,k) at offset (t*G+g)*K+k).
  *  - BF16 is passed as 16-bit patterns, FP8 e4m3 codes and E8M0 scale bytes as
@@ -258,6 +259,31 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t w_elem
 mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w,
                     const uint8_t* w_scale, int32_t w_elem_bytes, int64_t N, void* out,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Scratch held by the library for mx_linear_noalloc: one copy per GPU the
+ * library runs on, kept until the process ends. */
+#define MX_LINEAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * mx_linear_noalloc -- mx_linear for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, branches, kernels and results as
+ * mx_linear, without the workspace: the branches that need one (the MXFP8
+ * copy of x on the block-scaled branch, the per-call BF16 weight of an
+ * unprepared unaligned FP8 weight) use a scratch array inside the library,
+ * MX_LINEAR_NOALLOC_SCRATCH_BYTES per GPU, whose device address is looked up
+ * on the first call on each device.  The call allocates nothing (no hipMalloc,
+ * no allocating library routine).
+ * Returns MX_ERR_INVALID_ARG if mx_linear_workspace_bytes(M, N, K,
+ * w_elem_bytes) exceeds the scratch size; otherwise as mx_linear.
+ * The scratch is shared by every call on one GPU and keeps the last call's
+ * contents (each call writes all it reads before reading it, so nothing needs
+ * clearing): calls that overlap on one GPU -- on different streams, or from
+ * different threads -- race on it and must be serialised by the caller.
+ */
+mx_status mx_linear_noalloc(const void* x, int64_t M, int64_t K, const void* w,
+                            const uint8_t* w_scale, int32_t w_elem_bytes, int64_t N, void* out,
+                            void* stream);
 
 /* ---------------------------------------------------- format converters */
 

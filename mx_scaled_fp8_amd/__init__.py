@@ -22,7 +22,8 @@ __all__ = [
     "MX_LINEAR_K_ALIGN", "MX_LINEAR_BLOCK", "MxError", "lib", "lib_path",
     "mx_probe", "mx_version", "mx_set_dry_run", "mx_get_counters", "mx_reset_counters",
     "mx_inv_rope_group_quant", "mx_bmm_a8w8_mxscale", "mx_dequant_mxfp8_to_bf16",
-    "mx_linear_dequant_at_load", "mx_linear_workspace_bytes", "mx_linear",
+    "mx_linear_dequant_at_load", "mx_linear_workspace_bytes", "mx_linear", "mx_linear_noalloc",
+    "MX_LINEAR_NOALLOC_SCRATCH_BYTES",
     "mx_inv_rope_bf16", "mx_bmm_bf16", "mx_woa_expand_scales", "MX_SCALE_E8M0", "MX_SCALE_F32",
     "mx_f32_pow2_to_e8m0", "mx_f32_pow2_to_e8m0_device", "mx_f32_to_e4m3_ocp",
     "mx_f32_to_e4m3_fnuz", "mx_f32_to_e4m3_device", "mx_e4m3_to_f32", "mx_e8m0_to_f32",
@@ -35,6 +36,7 @@ MX_ROPE_INTERLEAVED, MX_ROPE_NEOX = 0, 1
 MX_SCALE_E8M0, MX_SCALE_F32 = 0, 1
 MX_LINEAR_K_ALIGN = 128
 MX_LINEAR_BLOCK = 32
+MX_LINEAR_NOALLOC_SCRATCH_BYTES = 32 << 20
 COUNTER_NAMES = ("quant", "bmm_large", "bmm_small", "dequant", "linear_bf16", "linear_fp8",
                  "linear_percall_dequant", "f32_to_e8m0_device", "f32_to_e4m3_device", "rope_bf16",
                  "bmm_bf16_large", "bmm_bf16_small", "expand_scales")
@@ -79,6 +81,7 @@ def lib():
             "mx_linear_dequant_at_load": (ctypes.c_int, [I64]),
             "mx_linear_workspace_bytes": (SZ, [I64, I64, I64, I32]),
             "mx_linear": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P, SZ, P]),
+            "mx_linear_noalloc": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P]),
             "mx_f32_pow2_to_e8m0": (ctypes.c_int, [P, P, I64]),
             "mx_f32_pow2_to_e8m0_device": (ctypes.c_int, [P, P, I64, P, P]),
             "mx_f32_to_e4m3_ocp": (ctypes.c_int, [P, P, I64]),
@@ -343,6 +346,32 @@ def mx_linear(x, w, w_scale=None, out=None, workspace=None):
     _check(lib().mx_linear(_dev(x, "x", 2), M, K, _dev(w, "w"),
                            _dev(w_scale, "w_scale", 1) if w_scale is not None else None, eb, N,
                            _dev(out, "out", 2), ws_ptr, ws_bytes, _stream(x)))
+    return out
+
+
+def mx_linear_noalloc(x, w, w_scale=None, out=None):
+    """As mx_linear, with the library's own scratch instead of a workspace:
+    the library allocates nothing (``out`` may be given to allocate nothing
+    here either).  Overlapping calls on one GPU race on that scratch."""
+    if x.dim() != 2 or w.dim() != 2:
+        raise ValueError(f"x must be [M,K] and w [N,K] (got {tuple(x.shape)} and {tuple(w.shape)})")
+    M, K = x.shape
+    N = w.shape[0]
+    eb = w.element_size()
+    _shape(w, (N, K), "w")
+    if eb == 1:
+        if w_scale is None:
+            raise ValueError("an FP8 weight needs w_scale [N, K/32]")
+        if K % MX_LINEAR_BLOCK:
+            raise ValueError(f"K = {K} is not a multiple of {MX_LINEAR_BLOCK}")
+        _numel(w_scale, N * (K // MX_LINEAR_BLOCK), "w_scale")
+    _numel(out, M * N, "out")
+    _same_device(x, ("w", w), ("w_scale", w_scale), ("out", out))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().mx_linear_noalloc(_dev(x, "x", 2), M, K, _dev(w, "w"),
+                                   _dev(w_scale, "w_scale", 1) if w_scale is not None else None, eb, N,
+                                   _dev(out, "out", 2), _stream(x)))
     return out
 
 

@@ -303,9 +303,14 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t w_elem
   return codes + static_cast<size_t>(M) * (K / MX_LINEAR_BLOCK);
 }
 
-mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const uint8_t* w_scale, int32_t w_elem_bytes,
-                    int64_t N, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "mx_linear";
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by mx_linear and mx_linear_noalloc (everything but
+// the workspace).
+mx_status linear_check(const char* fn, const void* x, int64_t M, int64_t K, const void* w, const uint8_t* w_scale,
+                       int32_t w_elem_bytes, int64_t N, void* out) {
   MX_CHECK(M >= 0 && N >= 0 && K > 0, "%s: M = %lld, N = %lld, K = %lld", fn, (long long)M, (long long)N,
            (long long)K);
   MX_CHECK(K % MX_LINEAR_BLOCK == 0, "%s: K = %lld is not a multiple of %d", fn, (long long)K, MX_LINEAR_BLOCK);
@@ -315,25 +320,25 @@ mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const ui
   MX_CHECK(M <= (int64_t(1) << 30) && K < (int64_t(1) << 31) && N * K < (int64_t(1) << 40) &&
                M * K < (int64_t(1) << 40),
            "%s: shape too large (M = %lld, N = %lld, K = %lld)", fn, (long long)M, (long long)N, (long long)K);
-  const bool fp8 = w_elem_bytes == 1;
-  const bool aligned_k = K % MX_LINEAR_K_ALIGN == 0;
-  if (fp8 && aligned_k && M > 64)
+  if (w_elem_bytes == 1 && K % MX_LINEAR_K_ALIGN == 0 && M > 64)
     return fail(MX_ERR_UNSUPPORTED, "%s: the block-scaled path takes M <= 64 rows (M = %lld)", fn, (long long)M);
-  const size_t need = mx_linear_workspace_bytes(M, N, K, w_elem_bytes);
-  if (M == 0 || N == 0) { clear_error(); return MX_OK; }
+  if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(x && w && out, "%s: null tensor pointer", fn);
-  MX_CHECK(!fp8 || w_scale, "%s: an FP8 weight needs w_scale", fn);
+  MX_CHECK(w_elem_bytes == 2 || w_scale, "%s: an FP8 weight needs w_scale", fn);
   MX_CHECK(aligned(x, 16) && aligned(w, 16) && aligned(out, 8), "%s: x and w must be 16-byte aligned", fn);
-  MX_CHECK(need == 0 || (workspace && workspace_bytes >= need && aligned(workspace, 16)),
-           "%s: this call needs a 16-byte aligned workspace of %zu bytes (got %zu)", fn, need, workspace_bytes);
-  MX_PREAMBLE();
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MX_OK;
+}
+
+// The three branches of the linear, on a checked call; `workspace` holds at
+// least mx_linear_workspace_bytes(M, N, K, w_elem_bytes), 16-byte aligned.
+mx_status linear_run(const void* x, int64_t M, int64_t K, const void* w, const uint8_t* w_scale,
+                     int32_t w_elem_bytes, int64_t N, void* out, void* workspace, hipStream_t s) {
   mx_status st;
-  if (!fp8) {
+  if (w_elem_bytes == 2) {
     // weight already BF16 (dequantised once at load)
     count(C_LINEAR_BF16);
     st = launch_gemm_bf16(x, w, out, M, N, K, s);
-  } else if (aligned_k) {
+  } else if (K % MX_LINEAR_K_ALIGN == 0) {
     // x -> MXFP8 (OCP, block 32, no rotation) into the workspace, then the
     // block-scaled FP8 GEMM
     count(C_LINEAR_FP8);
@@ -350,10 +355,80 @@ mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const ui
     // an FP8 weight with K % 128 != 0 that was not prepared at load: dequantise
     // it into the workspace on this call; it never reaches the scaled GEMM
     count(C_LINEAR_PERCALL);
-    void* wb = workspace;
-    st = launch_dequant(static_cast<const uint8_t*>(w), w_scale, wb, N, K, MX_LINEAR_BLOCK, s);
-    if (st == MX_OK) st = launch_gemm_bf16(x, wb, out, M, N, K, s);
+    st = launch_dequant(static_cast<const uint8_t*>(w), w_scale, workspace, N, K, MX_LINEAR_BLOCK, s);
+    if (st == MX_OK) st = launch_gemm_bf16(x, workspace, out, M, N, K, s);
   }
+  return st;
+}
+
+// Scratch of mx_linear_noalloc: one copy per GPU, in the code object, held
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not the device array; its device address comes from hipGetSymbolAddress,
+// once per device (scratch_on_current_device).
+constexpr size_t kScratchBytes = size_t(MX_LINEAR_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mx_status scratch_on_current_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MX_ERR_UNSUPPORTED, "no HIP device is present");
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(MX_ERR_INVALID_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MX_ERR_HIP, "mx_linear_noalloc: hipGetSymbolAddress of the scratch array failed on device %d: %s",
+                  dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w, const uint8_t* w_scale, int32_t w_elem_bytes,
+                    int64_t N, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "mx_linear";
+  mx_status st = linear_check(fn, x, M, K, w, w_scale, w_elem_bytes, N, out);
+  if (st != MX_OK) return st;
+  if (M == 0 || N == 0) { clear_error(); return MX_OK; }
+  const size_t need = mx_linear_workspace_bytes(M, N, K, w_elem_bytes);
+  MX_CHECK(need == 0 || (workspace && workspace_bytes >= need && aligned(workspace, 16)),
+           "%s: this call needs a 16-byte aligned workspace of %zu bytes (got %zu)", fn, need, workspace_bytes);
+  MX_PREAMBLE();
+  st = linear_run(x, M, K, w, w_scale, w_elem_bytes, N, out, workspace, static_cast<hipStream_t>(stream));
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_linear_noalloc(const void* x, int64_t M, int64_t K, const void* w, const uint8_t* w_scale,
+                            int32_t w_elem_bytes, int64_t N, void* out, void* stream) {
+  const char* fn = "mx_linear_noalloc";
+  mx_status st = linear_check(fn, x, M, K, w, w_scale, w_elem_bytes, N, out);
+  if (st != MX_OK) return st;
+  if (M == 0 || N == 0) { clear_error(); return MX_OK; }
+  const size_t need = mx_linear_workspace_bytes(M, N, K, w_elem_bytes);
+  if (need > kScratchBytes)
+    return fail(MX_ERR_INVALID_ARG,
+                "%s: this call needs %zu bytes of scratch, more than the library's %zu (M = %lld, N = %lld, "
+                "K = %lld); use mx_linear with a workspace",
+                fn, need, kScratchBytes, (long long)M, (long long)N, (long long)K);
+  MX_PREAMBLE();
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_on_current_device(&ws);
+    if (st != MX_OK) return st;
+  }
+  st = linear_run(x, M, K, w, w_scale, w_elem_bytes, N, out, ws, static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();
   return st;
 }

@@ -257,3 +257,18 @@ def test_no_device_means_unsupported():
         pytest.skip("a GPU is present")
     assert _quant() == mx.MX_ERR_UNSUPPORTED
     assert mx.lib().mx_probe(0) == mx.MX_ERR_UNSUPPORTED
+
+
+def test_linear_noalloc_validation(dry):
+    def f(M=64, K=576, eb=1, N=4096, **kw):
+        return _call("mx_linear_noalloc", kw.get("x", FAKE), M, K, kw.get("w", FAKE), kw.get("s", FAKE), eb, N,
+                     kw.get("o", FAKE), None)
+    assert f() == mx.MX_OK                                           # 4.7 MB of per-call dequant: fits
+    assert f(K=1152) == mx.MX_OK
+    assert f(eb=2) == mx.MX_OK
+    assert f(N=16384, K=1056) == mx.MX_ERR_INVALID_ARG               # 34.6 MB > the 32 MiB scratch
+    assert f(N=16384, K=1056, eb=2) == mx.MX_OK                      # a BF16 weight needs no scratch
+    assert f(K=1152, M=65) == mx.MX_ERR_UNSUPPORTED
+    assert f(K=100) == mx.MX_ERR_INVALID_ARG
+    assert f(s=None) == mx.MX_ERR_INVALID_ARG
+    assert f(M=0, x=None) == mx.MX_OK
