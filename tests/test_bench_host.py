@@ -44,3 +44,27 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one MI355X" in r.stderr
+
+
+def test_parity_record_flags_each_kind_of_mismatch():
+    """The bench's parity record on planted differences: identical results
+    pass; a scale byte, a code two steps away, too many one-step codes, or a
+    GEMM output outside 2^-7 |ref| + 1e-3 rms(ref) each fail it."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    rq = rng.integers(0, 0x7E, (64, 256), dtype=np.uint8)
+    rs = rng.integers(110, 130, (64, 2), dtype=np.uint8)
+    ref = rng.standard_normal((64, 32))
+    bits = (ref.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)     # truncation: within 2^-7
+    ok = bench.parity_record(rq.copy(), rs.copy(), bits, rq, rs, ref, "same")
+    assert ok["pass"] and ok["outputs_outside_bound"] == 0 and ok["worst_err_over_bound"] <= 1
+
+    s2 = rs.copy(); s2[3, 1] ^= 1
+    assert not bench.parity_record(rq, s2, bits, rq, rs, ref, "scale")["pass"]
+    q2 = rq.copy(); q2[5, 7] = rq[5, 7] + 2
+    assert not bench.parity_record(q2, rs, bits, rq, rs, ref, "code two steps")["pass"]
+    q3 = rq.copy(); q3[0, :3] = rq[0, :3] + 1                                     # 3 > 1e-4 * 16384
+    assert not bench.parity_record(q3, rs, bits, rq, rs, ref, "too many one-step codes")["pass"]
+    b2 = bits.copy(); b2[2, 2] ^= 0x0040                                           # a mantissa bit high up
+    r = bench.parity_record(None, None, b2, None, None, ref, "gemm")
+    assert not r["pass"] and r["outputs_outside_bound"] >= 1
