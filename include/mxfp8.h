@@ -252,9 +252,8 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t w_elem
  * workspace device, at least mx_linear_workspace_bytes(M, N, K, w_elem_bytes),
  *          16-byte aligned (may be NULL when that is 0).
  * Requires: M, N >= 0, K > 0, K % 32 == 0, N % 16 == 0, x/w 16-byte aligned,
- * out 8-byte aligned.  The block-scaled FP8 branch takes M <= 64 rows (a decode
- * batch); K above 19,584 returns MX_ERR_UNSUPPORTED there (the scale rows no
- * longer fit the kernel's LDS).
+ * out 8-byte aligned.  Any M: up to 64 rows (a decode batch) run on kernels that
+ * keep the weight streaming, more rows (a prefill chunk) on 256 x 256 tiles.
  */
 mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w,
                     const uint8_t* w_scale, int32_t w_elem_bytes, int64_t N, void* out,

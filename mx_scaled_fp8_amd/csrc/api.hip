@@ -320,8 +320,6 @@ mx_status linear_check(const char* fn, const void* x, int64_t M, int64_t K, cons
   MX_CHECK(M <= (int64_t(1) << 30) && K < (int64_t(1) << 31) && N * K < (int64_t(1) << 40) &&
                M * K < (int64_t(1) << 40),
            "%s: shape too large (M = %lld, N = %lld, K = %lld)", fn, (long long)M, (long long)N, (long long)K);
-  if (w_elem_bytes == 1 && K % MX_LINEAR_K_ALIGN == 0 && M > 64)
-    return fail(MX_ERR_UNSUPPORTED, "%s: the block-scaled path takes M <= 64 rows (M = %lld)", fn, (long long)M);
   if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(x && w && out, "%s: null tensor pointer", fn);
   MX_CHECK(w_elem_bytes == 2 || w_scale, "%s: an FP8 weight needs w_scale", fn);
@@ -340,15 +338,15 @@ mx_status linear_run(const void* x, int64_t M, int64_t K, const void* w, const u
     st = launch_gemm_bf16(x, w, out, M, N, K, s);
   } else if (K % MX_LINEAR_K_ALIGN == 0) {
     // x -> MXFP8 (OCP, block 32, no rotation) into the workspace, then the
-    // block-scaled FP8 GEMM
+    // block-scaled FP8 GEMM (up to 16 rows and K <= 4096 both in one kernel)
     count(C_LINEAR_FP8);
     const uint8_t* w8 = static_cast<const uint8_t*>(w);
-    if (!launch_linear_mx32_fused(x, w8, w_scale, out, M, N, K, s, &st)) {
+    if (M > 16 || !launch_linear_mx32_fused(x, w8, w_scale, out, M, N, K, s, &st)) {
       uint8_t* xq = static_cast<uint8_t*>(workspace);
       uint8_t* xs = xq + (static_cast<size_t>(M) * K + 15) / 16 * 16;
       st = launch_quant(x, nullptr, nullptr, nullptr, 0, M, 1, static_cast<int32_t>(K), 0, MX_ROPE_INTERLEAVED,
                         MX_LINEAR_BLOCK, MX_FP8_E4M3_OCP, xq, xs, s);
-      if (st == MX_OK && !launch_gemm_mx32_wres(xq, xs, w8, w_scale, out, M, N, K, s, &st))
+      if (st == MX_OK && (M > 64 || !launch_gemm_mx32_wres(xq, xs, w8, w_scale, out, M, N, K, s, &st)))
         st = launch_gemm_mx32(xq, xs, w8, w_scale, out, M, N, K, s);
     }
   } else {

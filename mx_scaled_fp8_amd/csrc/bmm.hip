@@ -44,7 +44,8 @@
 //    double-buffered in registers, partial sums reduced through LDS.
 //  * gemm_mx32_dma_kernel: the MXFP8 linear's block-32 GEMM (M <= 64) on the
 //    decode kernel's ring, for the shapes the weight-resident kernels of
-//    linear_mx32.hip do not take.
+//    linear_mx32.hip do not take; more rows run on bmm_large_kernel with
+//    block-32 scales.
 #include <algorithm>
 #include <type_traits>
 
@@ -128,14 +129,23 @@ __device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], co
                                                              static_cast<int>(sav));
 }
 
-template <bool A_FNUZ>
+// SB is the K extent of one scale byte: 128 (the wo_a layout, one scale per
+// stage and row) or 32 (the MXFP8 linear's blocks, four per stage and row).
+// With 32, the scale a 32x32x64 MFMA applies to the K-block of lane group q
+// is the block's own: in 64-K half h of a stage, lane group q passes block
+// 2h + q (the lane data layout is the same for both: byte j of a half is the
+// instruction's k = j).
+template <bool A_FNUZ, int SB>
 __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
+  static_assert(SB == 128 || SB == 32, "scale block");
+  constexpr int kSPS = kBK / SB;                 // scale blocks per stage and row: 1 or 4
+  constexpr int kWin = kScaleWin / kSPS;         // stages per scale window: 32 or 8
   // stage buffers: [W tile 256 x 128 B | A tile 256 x 128 B]
   __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kOpBytes];
-  // scales of a window of stages, [stage][W|A][wave half][row % 32][tile]:
+  // scales of a window of stages, [stage][block][W|A][wave half][row % 32][tile]:
   // one 4-byte read gives a lane the scales of its 4 tiles of one operand
-  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kScaleWin][2][2][32][4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sc[kWin][kSPS][2][2][32][4];
 
   // XCD-aware work id: workgroup i runs on XCD i % 8
   const int xcd = blockIdx.x & 7;
@@ -157,7 +167,7 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   // activation panel (same tt) or a weight tile (same nt) stay within a few
   // stages of each other and still find the shared rows in L2.  Rotation
   // needs every scale in one window, so it is used when K fits one.
-  const int kb0 = KB <= kScaleWin ? (tt + nt) % KB : 0;
+  const int kb0 = KB <= kWin ? (tt + nt) % KB : 0;
   const uint32_t rowA = static_cast<uint32_t>(p.G) * p.K;   // activation row stride
 
   // LDS-DMA sources: wave `wave` fills rows it*32 + wave*8 + lane/8 (it =
@@ -220,21 +230,27 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   // scale staging: thread tid owns W row tid and A row tid.  LDS slot s of
   // the window holds stage s of the window (the actual stage, not the loop
   // index: with the rotation, loop stage kb reads slot (kb + kb0) mod KB).
-  const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
-  const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * KB;
-  uint8_t* sc_dst = &lds_sc[0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
-  constexpr int kScStep = 2 * 2 * 32 * 4;
+  const int SPR = KB * kSPS;                   // scale bytes per row
+  const uint8_t* scW = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * SPR;
+  const uint8_t* scA = p.sa + (static_cast<size_t>(t0 + min(tid, limA)) * p.G + g) * SPR;
+  uint8_t* sc_dst = &lds_sc[0][0][0][tid >> 7][tid & 31][(tid >> 5) & 3];
+  constexpr int kScBlk = 2 * 2 * 32 * 4;
+  constexpr int kScStep = kSPS * kScBlk;
   constexpr int kScOp = 2 * 32 * 4;
-  auto put_scales = [&](int s, uint32_t bw, uint32_t ba) {
-    sc_dst[s * kScStep] = static_cast<uint8_t>(bw);
-    sc_dst[s * kScStep + kScOp] = static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(static_cast<int>(ba)) : ba);
+  auto put_scales = [&](int s, int blk, uint32_t bw, uint32_t ba) {
+    sc_dst[s * kScStep + blk * kScBlk] = static_cast<uint8_t>(bw);
+    sc_dst[s * kScStep + blk * kScBlk + kScOp] =
+        static_cast<uint8_t>(A_FNUZ ? fnuz_scale_to_ocp(static_cast<int>(ba)) : ba);
   };
   auto stage_scales_serial = [&](int first) {   // few registers: for the loop (K > one window)
-    const int n = min(kScaleWin, KB - first);
-    for (int s = 0; s < n; ++s) put_scales(s, scW[first + s], scA[first + s]);
+    const int n = min(kWin, KB - first);
+    for (int s = 0; s < n; ++s)
+#pragma unroll
+      for (int b = 0; b < kSPS; ++b) put_scales(s, b, scW[(first + s) * kSPS + b], scA[(first + s) * kSPS + b]);
   };
   auto stage_scales_first = [&]() {             // the first window, before the loop
-    if ((KB & 15) == 0 && ((reinterpret_cast<uintptr_t>(scW) | reinterpret_cast<uintptr_t>(scA)) & 15) == 0) {
+    if (SB == 128 && (KB & 15) == 0 &&
+        ((reinterpret_cast<uintptr_t>(scW) | reinterpret_cast<uintptr_t>(scA)) & 15) == 0) {
       // two 16-byte loads per row instead of 32 byte loads
       const uint4 w0 = *reinterpret_cast<const uint4*>(scW), a0 = *reinterpret_cast<const uint4*>(scA);
       uint4 w1 = make_uint4(0, 0, 0, 0), a1 = w1;
@@ -246,25 +262,41 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
       const uint32_t aw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
       for (int s = 0; s < kScaleWin; ++s)        // slots past the last stage are never read
-        put_scales(s, (ww[s >> 2] >> (8 * (s & 3))) & 0xFF, (aw[s >> 2] >> (8 * (s & 3))) & 0xFF);
+        put_scales(s, 0, (ww[s >> 2] >> (8 * (s & 3))) & 0xFF, (aw[s >> 2] >> (8 * (s & 3))) & 0xFF);
     } else {
-      uint8_t bw[kScaleWin], ba[kScaleWin];      // all loads first, then the LDS writes
+      uint8_t bw[kWin * kSPS], ba[kWin * kSPS];  // all loads first, then the LDS writes
 #pragma unroll
-      for (int s = 0; s < kScaleWin; ++s) {
+      for (int s = 0; s < kWin; ++s) {
         const int ks = min(s, KB - 1);           // slots past the last stage read a valid byte
-        bw[s] = scW[ks];
-        ba[s] = scA[ks];
+#pragma unroll
+        for (int b = 0; b < kSPS; ++b) {
+          bw[s * kSPS + b] = scW[ks * kSPS + b];
+          ba[s * kSPS + b] = scA[ks * kSPS + b];
+        }
       }
 #pragma unroll
-      for (int s = 0; s < kScaleWin; ++s) put_scales(s, bw[s], ba[s]);
+      for (int s = 0; s < kWin; ++s)
+#pragma unroll
+        for (int b = 0; b < kSPS; ++b) put_scales(s, b, bw[s * kSPS + b], ba[s * kSPS + b]);
     }
   };
-  auto read_scales = [&](int kb, uint32_t& swv, uint32_t& sav) {
+  // the scale words of loop stage kb: [h] for 64-K half h (one word for both
+  // halves when SB = 128; block 2h + q2 of the stage when SB = 32)
+  constexpr int H1 = kSPS == 1 ? 0 : 1;         // index of half 1's words
+  auto read_scales = [&](int kb, uint32_t (&swv)[2], uint32_t (&sav)[2]) {
     int ks = kb + kb0;                           // the stage loop index kb covers
     ks -= ks >= KB ? KB : 0;
-    const int s = ks & (kScaleWin - 1);
-    swv = *reinterpret_cast<const uint32_t*>(&lds_sc[s][0][wn][r32][0]);
-    sav = *reinterpret_cast<const uint32_t*>(&lds_sc[s][1][wt][r32][0]);
+    const int s = ks & (kWin - 1);
+    if constexpr (kSPS == 1) {
+      swv[0] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][0][0][wn][r32][0]);
+      sav[0] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][0][1][wt][r32][0]);
+    } else {
+      const int q = lane >> 5;
+      swv[0] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][q][0][wn][r32][0]);
+      sav[0] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][q][1][wt][r32][0]);
+      swv[1] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][2 + q][0][wn][r32][0]);
+      sav[1] = *reinterpret_cast<const uint32_t*>(&lds_sc[s][2 + q][1][wt][r32][0]);
+    }
   };
 
   v16f acc[4][4];
@@ -327,10 +359,10 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   // followed a full wait) no DMA is pending: the compiler then sees, in
   // straight-line code, that the reads of one buffer never alias the DMA into
   // the other and adds no wait of its own.
-  uint32_t swv, sav;
+  uint32_t swv[2], sav[2];
   auto front = [&](const uint8_t* cur, int kb, bool new_window) {
     __builtin_amdgcn_sched_barrier(0);
-    mma_half(fw[0], fa[0], swv, sav);
+    mma_half(fw[0], fa[0], swv[0], sav[0]);
     read_half(cur, ch10, ch11, fw[1], fa[1]);
     // reads early in the half (two per MFMA), so they land before the half ends
 #pragma unroll
@@ -351,9 +383,9 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
   };
   auto back = [&](uint8_t* cur, const uint8_t* nxt, int kb, bool dma) {
     if (dma) issue(cur, kb + 2);
-    uint32_t swv1, sav1;
+    uint32_t swv1[2], sav1[2];
     read_scales(kb + 1, swv1, sav1);
-    mma_half(fw[1], fa[1], swv, sav);
+    mma_half(fw[1], fa[1], swv[H1], sav[H1]);
     read_half(nxt, ch00, ch01, fw[0], fa[0]);
     // one DMA instruction per MFMA: a burst of 16 would stall this wave on the
     // texture-address unit, which takes the four waves' DMA at about the rate
@@ -371,11 +403,14 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     }
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    swv = swv1;
-    sav = sav1;
+#pragma unroll
+    for (int h = 0; h <= H1; ++h) {
+      swv[h] = swv1[h];
+      sav[h] = sav1[h];
+    }
   };
   auto window_at = [&](int kb) {             // front(kb) restages scales for stage kb+1
-    return KB > kScaleWin && (kb + 1) % kScaleWin == 0 && kb + 1 < KB;
+    return KB > kWin && (kb + 1) % kWin == 0 && kb + 1 < KB;
   };
 
   // prologue: scales of the first window, stages 0 and 1 in flight, half 0 of
@@ -404,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
     back(st0, st1, kb, false);
     front(st1, kb + 1, false);
   }
-  mma_half(fw[1], fa[1], swv, sav);             // second half of the last stage
+  mma_half(fw[1], fa[1], swv[H1], sav[H1]);     // second half of the last stage
   __builtin_amdgcn_s_waitcnt(kWaitAll);         // no DMA or LDS read outlives the loop
 
   // Epilogue straight from the accumulators.  Lane holds tile element (t, n)
@@ -1435,34 +1470,46 @@ mx_status launch_bmm(const uint8_t* a, const uint8_t* sa, int32_t a_fmt, const u
     p.wg_per_xcd = 0;
     const int grid = p.per_xcd * 8;
     if (fnuz)
-      bmm_large_kernel<true><<<grid, 256, 0, stream>>>(p);
+      bmm_large_kernel<true, 128><<<grid, 256, 0, stream>>>(p);
     else
-      bmm_large_kernel<false><<<grid, 256, 0, stream>>>(p);
+      bmm_large_kernel<false, 128><<<grid, 256, 0, stream>>>(p);
   }
   count(C_BMM_LARGE);
   return launch_status("mx_bmm_a8w8_mxscale");
 }
 
 // Block-32 scaled FP8 GEMM for the MXFP8 linear: out[M,N] = xq[M,K] * W[N,K]^T
-// with scales [M,K/32] and [N,K/32], M <= 64.
+// with scales [M,K/32] and [N,K/32], any M >= 1.
 mx_status launch_gemm_mx32(const uint8_t* xq, const uint8_t* xs, const uint8_t* w, const uint8_t* sw, void* out,
                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return MX_OK;
-  // the LDS-DMA ring (M = 64, N = 4096: 10.9 -> 7.8 us at K = 1152 against
-  // bmm_small_kernel<1, 32>)
-  if (K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
+  if (M <= 64 && K <= 8192 && aligned(xs, 4) && aligned(sw, 4)) {
+    // the LDS-DMA ring (M = 64, N = 4096: 10.9 -> 7.8 us at K = 1152 against
+    // bmm_small_kernel<1, 32>)
     SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
                 static_cast<int>(K), static_cast<int>((N + kLinRowsW - 1) / kLinRowsW)};
     gemm_mx32_dma_kernel<<<s.n_groups, 256, 0, stream>>>(s);
     return launch_status("mx_linear (block-scaled FP8 GEMM)");
   }
-  if (small_scale_lds<1, 32>(static_cast<int>(K)) > kSmallScaleLdsMax)
-    return fail(MX_ERR_UNSUPPORTED, "mx_linear: K = %lld is too large for the block-scaled FP8 path (at most %zu)",
-                static_cast<long long>(K), kSmallScaleLdsMax / 80 * 32);
-  SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
-              static_cast<int>(K), static_cast<int>((N + 15) / 16)};
-  launch_small<1, 32>(s, false, stream);
-  return launch_status("mx_linear (block-scaled FP8 GEMM)");
+  if (M <= 64 && small_scale_lds<1, 32>(static_cast<int>(K)) <= kSmallScaleLdsMax) {
+    SmallArgs s{xq, xs, w, sw, static_cast<uint16_t*>(out), static_cast<int>(M), 1, static_cast<int>(N),
+                static_cast<int>(K), static_cast<int>((N + 15) / 16)};
+    launch_small<1, 32>(s, false, stream);
+    return launch_status("mx_linear (block-scaled FP8 GEMM)");
+  }
+  // more rows (or K past the small kernels' scale staging): 256 x 256 tiles
+  // of bmm_large_kernel with block-32 scales, one group
+  LargeArgs p;
+  p.a = xq; p.sa = xs; p.w = w; p.sw = sw;
+  p.out = static_cast<uint16_t*>(out);
+  p.T = static_cast<int>(M); p.G = 1; p.N = static_cast<int>(N); p.K = static_cast<int>(K);
+  p.tiles_t = static_cast<int>((M + kLT - 1) / kLT);
+  p.tiles_n = static_cast<int>((N + kLN - 1) / kLN);
+  p.total_tiles = p.tiles_t * p.tiles_n;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  p.wg_per_xcd = 0;
+  bmm_large_kernel<false, 32><<<p.per_xcd * 8, 256, 0, stream>>>(p);
+  return launch_status("mx_linear (block-scaled FP8 GEMM, 256 x 256 tiles)");
 }
 
 // BF16 decode batch of the BF16 wo_a arm on the decode kernel: x [T, G, K],

@@ -188,7 +188,7 @@ def test_linear_validation(dry):
     assert f(N=100) == mx.MX_ERR_INVALID_ARG
     assert f(eb=4) == mx.MX_ERR_INVALID_ARG
     assert f(s=None) == mx.MX_ERR_INVALID_ARG
-    assert f(K=1152, M=65) == mx.MX_ERR_UNSUPPORTED                # the caller's cue to fall back
+    assert f(K=1152, M=65, wsb=65 * 1152 * 2) == mx.MX_OK             # prefill-sized M: the tiled kernel
     # K on its own past 2^31 (N small enough for N*K): rejected before any
     # kernel narrows it to 32 bits
     assert f(K=1 << 31, N=16, M=1, eb=2, ws=None, wsb=0) == mx.MX_ERR_INVALID_ARG
@@ -268,7 +268,7 @@ def test_linear_noalloc_validation(dry):
     assert f(eb=2) == mx.MX_OK
     assert f(N=16384, K=1056) == mx.MX_ERR_INVALID_ARG               # 34.6 MB > the 32 MiB scratch
     assert f(N=16384, K=1056, eb=2) == mx.MX_OK                      # a BF16 weight needs no scratch
-    assert f(K=1152, M=65) == mx.MX_ERR_UNSUPPORTED
+    assert f(K=1152, M=8192) == mx.MX_OK                             # no scratch needed beyond 32 MiB
     assert f(K=100) == mx.MX_ERR_INVALID_ARG
     assert f(s=None) == mx.MX_ERR_INVALID_ARG
     assert f(M=0, x=None) == mx.MX_OK
