@@ -91,9 +91,10 @@ void mx_set_dry_run(int on);
 /* Launch counters, in this order: quant, bmm (large tiles), bmm (small T),
  * dequant, linear BF16 branch (prepared weight), linear FP8 branch, linear
  * per-call-dequant branch, f32->e8m0 device, e4m3 encode device, inverse RoPE
- * to BF16, BF16 bmm (large tiles), BF16 bmm (small T), wo_a scale expansion.
+ * to BF16, BF16 bmm (large tiles), BF16 bmm (small T), wo_a scale expansion,
+ * single-kernel wo_a.
  * `out` gets min(n, MX_NUM_COUNTERS) values; returns MX_NUM_COUNTERS. */
-#define MX_NUM_COUNTERS 13
+#define MX_NUM_COUNTERS 14
 int mx_get_counters(uint64_t* out, int n);
 void mx_reset_counters(void);
 
@@ -149,6 +150,35 @@ mx_status mx_inv_rope_group_quant(const void* x, const int64_t* positions,
 mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t a_fmt,
                               const uint8_t* w, const uint8_t* w_scale, void* out,
                               int64_t T, int32_t G, int32_t N, int32_t K, void* stream);
+
+/*
+ * mx_wo_a_fused -- the whole FP8 wo_a step in one kernel: inverse RoPE,
+ * per-token group-128 E8M0 FP8 quantisation and the batched a8w8 MX-scale
+ * GEMM, the quantised activation never leaving the compute unit ([WOA],
+ * Summary: an inverse RoPE fused with per-token E8M0 group quantisation,
+ * then the MX batched GEMM with the checkpoint's FP8 weight; here the two are
+ * one pass).
+ *
+ * out = mx_bmm_a8w8_mxscale(q, scale, OCP, w, w_scale) with (q, scale) =
+ * mx_inv_rope_group_quant(x, ..., group 128, OCP) -- the same codes and
+ * scales, so the same values as the two calls (up to the order of the fp32
+ * sums).  A token whose position is outside [0, max_pos) has NaN outputs.
+ * x, positions, cos, sin, max_pos, T, H, D, rope_dim, rope_style: as for
+ *           mx_inv_rope_group_quant; the token row [H*D] is read as [G, K]
+ *           with K = H*D/G.
+ * w        device u8 [G, N, K] OCP e4m3.   w_scale device u8 [G, N, K/128].
+ * out      device BF16 [T, G, N].
+ * Requires: T >= 0 (0 is a no-op), G >= 1, H*D % G == 0, K % 128 == 0,
+ * K <= 4096, D % 128 == 0, rope_dim % 16 == 0 and rope_dim <= min(D, 128)
+ * (split halves: rope_dim in {16, 32, 64, 128}), N >= 1 with N % 16 == 0,
+ * x, w and out 16-byte aligned, positions 8-byte aligned, cos/sin 8-byte
+ * aligned (16 for split halves), max_pos >= 1 when rope_dim > 0.  Other
+ * shapes return MX_ERR_UNSUPPORTED (the two calls serve them).
+ */
+mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos,
+                        const void* sin, int64_t max_pos, int64_t T, int32_t H, int32_t D,
+                        int32_t rope_dim, int32_t rope_style, const uint8_t* w,
+                        const uint8_t* w_scale, void* out, int32_t G, int32_t N, void* stream);
 
 /*
  * mx_woa_expand_scales -- checkpoint weight scales of wo_a -> the layout the

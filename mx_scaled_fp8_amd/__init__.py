@@ -21,7 +21,7 @@ __all__ = [
     "MX_FP8_E4M3_OCP", "MX_FP8_E4M3_FNUZ", "MX_ROPE_INTERLEAVED", "MX_ROPE_NEOX",
     "MX_LINEAR_K_ALIGN", "MX_LINEAR_BLOCK", "MxError", "lib", "lib_path",
     "mx_probe", "mx_version", "mx_set_dry_run", "mx_get_counters", "mx_reset_counters",
-    "mx_inv_rope_group_quant", "mx_bmm_a8w8_mxscale", "mx_dequant_mxfp8_to_bf16",
+    "mx_inv_rope_group_quant", "mx_bmm_a8w8_mxscale", "mx_wo_a_fused", "mx_dequant_mxfp8_to_bf16",
     "mx_linear_dequant_at_load", "mx_linear_workspace_bytes", "mx_linear", "mx_linear_noalloc",
     "MX_LINEAR_NOALLOC_SCRATCH_BYTES",
     "mx_inv_rope_bf16", "mx_bmm_bf16", "mx_woa_expand_scales", "MX_SCALE_E8M0", "MX_SCALE_F32",
@@ -39,7 +39,7 @@ MX_LINEAR_BLOCK = 32
 MX_LINEAR_NOALLOC_SCRATCH_BYTES = 32 << 20
 COUNTER_NAMES = ("quant", "bmm_large", "bmm_small", "dequant", "linear_bf16", "linear_fp8",
                  "linear_percall_dequant", "f32_to_e8m0_device", "f32_to_e4m3_device", "rope_bf16",
-                 "bmm_bf16_large", "bmm_bf16_small", "expand_scales")
+                 "bmm_bf16_large", "bmm_bf16_small", "expand_scales", "wo_a_fused")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8.so")
@@ -78,6 +78,7 @@ def lib():
             "mx_inv_rope_bf16": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, I32, P, P]),
             "mx_bmm_bf16": (ctypes.c_int, [P, P, P, I64, I32, I32, I32, P]),
             "mx_woa_expand_scales": (ctypes.c_int, [P, I32, I32, I32, I32, I32, P, P, P]),
+            "mx_wo_a_fused": (ctypes.c_int, [P, P, P, P, I64, I64, I32, I32, I32, I32, P, P, P, I32, I32, P]),
             "mx_linear_dequant_at_load": (ctypes.c_int, [I64]),
             "mx_linear_workspace_bytes": (SZ, [I64, I64, I64, I32]),
             "mx_linear": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P, SZ, P]),
@@ -236,6 +237,33 @@ def mx_bmm_a8w8_mxscale(a, a_scale, w, w_scale, a_fmt=MX_FP8_E4M3_OCP, out=None)
         out = torch.empty((T, G, N), dtype=torch.bfloat16, device=a.device)
     _check(lib().mx_bmm_a8w8_mxscale(_dev(a, "a", 1), _dev(a_scale, "a_scale", 1), a_fmt, _dev(w, "w", 1),
                                      _dev(w_scale, "w_scale", 1), _dev(out, "out", 2), T, G, N, K, _stream(a)))
+    return out
+
+
+def mx_wo_a_fused(x, positions, cos, sin, H, D, rope_dim, w, w_scale, rope_style=MX_ROPE_INTERLEAVED, out=None):
+    """x BF16 [T, H*D], w uint8 [G, N, K] (K = H*D/G), w_scale [G, N, K/128] ->
+    BF16 [T, G, N]: inverse RoPE, group-128 quantisation and the MX-scale GEMM
+    in one kernel."""
+    if x.dim() != 2 or w.dim() != 3:
+        raise ValueError(f"x must be [T, H*D] and w [G,N,K] (got {tuple(x.shape)} and {tuple(w.shape)})")
+    T = x.shape[0]
+    _shape(x, (T, H * D), "x")
+    G, N, K = w.shape
+    if G * K != H * D:
+        raise ValueError(f"w has shape {tuple(w.shape)}: G*K must be H*D = {H * D}")
+    if K % 128:
+        raise ValueError(f"K = {K} is not a multiple of 128")
+    _numel(w_scale, G * N * (K // 128), "w_scale")
+    max_pos = _rope_args(x, positions, cos, sin, T, rope_dim)
+    _numel(out, T * G * N, "out")
+    _same_device(x, ("w", w), ("w_scale", w_scale), ("out", out))
+    if out is None:
+        out = torch.empty((T, G, N), dtype=torch.bfloat16, device=x.device)
+    _check(lib().mx_wo_a_fused(
+        _dev(x, "x", 2), _dev(positions, "positions", 8) if positions is not None else None,
+        _dev(cos, "cos", 2) if cos is not None else None, _dev(sin, "sin", 2) if sin is not None else None,
+        max_pos, T, H, D, rope_dim, rope_style, _dev(w, "w", 1), _dev(w_scale, "w_scale", 1), _dev(out, "out", 2),
+        G, N, _stream(x)))
     return out
 
 

@@ -37,6 +37,10 @@ mx_status launch_bmm_bf16(const void* x, const void* w, void* out, int64_t T, in
                           hipStream_t stream);
 mx_status launch_expand_scales(const void* in, int32_t kind, int32_t block_n, int32_t G, int32_t N, int32_t K,
                                uint8_t* out, int32_t* reject_count, hipStream_t stream);
+mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* cos, const void* sin,
+                           int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
+                           const uint8_t* w, const uint8_t* w_scale, void* out, int32_t G, int32_t N,
+                           hipStream_t stream);
 
 namespace {
 
@@ -220,6 +224,48 @@ mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t 
   MX_CHECK(aligned(out, 16), "%s: out must be 16-byte aligned", fn);
   MX_PREAMBLE();
   const mx_status st = launch_bmm(a, a_scale, a_fmt, w, w_scale, out, T, G, N, K, static_cast<hipStream_t>(stream));
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos, const void* sin, int64_t max_pos,
+                        int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t rope_style, const uint8_t* w,
+                        const uint8_t* w_scale, void* out, int32_t G, int32_t N, void* stream) {
+  const char* fn = "mx_wo_a_fused";
+  MX_CHECK(T >= 0 && T < (int64_t(1) << 31), "%s: T = %lld out of range", fn, (long long)T);
+  MX_CHECK(H > 0 && D > 0 && G >= 1 && N >= 1, "%s: H = %d, D = %d, G = %d, N = %d must be positive", fn, H, D, G,
+           N);
+  const int64_t L = static_cast<int64_t>(H) * D;
+  MX_CHECK(L % G == 0, "%s: H*D = %lld is not a multiple of G = %d", fn, (long long)L, G);
+  MX_CHECK(L < (int64_t(1) << 23), "%s: H*D = %lld is too large", fn, (long long)L);
+  const int64_t K = L / G;
+  MX_CHECK(K % MX_WOA_GROUP == 0, "%s: K = %lld is not a multiple of 128", fn, (long long)K);
+  MX_CHECK(N % 16 == 0, "%s: N = %d is not a multiple of 16", fn, N);
+  MX_CHECK(rope_dim >= 0 && rope_dim <= D && rope_dim % 16 == 0, "%s: rope_dim = %d (multiple of 16, <= D = %d)",
+           fn, rope_dim, D);
+  MX_CHECK(rope_style == MX_ROPE_INTERLEAVED || rope_style == MX_ROPE_NEOX, "%s: unknown rope style %d", fn,
+           rope_style);
+  // shapes the one-kernel path does not take: the two calls serve them
+  if (K > 4096 || D % 128 != 0 || rope_dim > 128 ||
+      (rope_style == MX_ROPE_NEOX && rope_dim > 0 && (rope_dim & (rope_dim - 1)) != 0))
+    return fail(MX_ERR_UNSUPPORTED,
+                "%s: K = %lld, D = %d, rope_dim = %d (style %d) not served in one kernel; use "
+                "mx_inv_rope_group_quant then mx_bmm_a8w8_mxscale",
+                fn, (long long)K, D, rope_dim, rope_style);
+  if (T == 0) { clear_error(); return MX_OK; }
+  MX_CHECK(x && w && w_scale && out, "%s: null tensor pointer", fn);
+  MX_CHECK(aligned(x, 16) && aligned(w, 16) && aligned(out, 16), "%s: x, w and out must be 16-byte aligned", fn);
+  if (rope_dim > 0) {
+    MX_CHECK(positions && cos && sin, "%s: rope_dim > 0 needs positions, cos and sin", fn);
+    MX_CHECK(max_pos >= 1, "%s: max_pos = %lld", fn, (long long)max_pos);
+    const uintptr_t ta = rope_style == MX_ROPE_NEOX ? 16 : 8;
+    MX_CHECK(aligned(cos, ta) && aligned(sin, ta) && aligned(positions, 8),
+             "%s: cos/sin must be %d-byte aligned, positions 8-byte aligned", fn, (int)ta);
+  }
+  MX_PREAMBLE();
+  count(C_WOA_FUSED);
+  const mx_status st = launch_woa_fused(x, positions, cos, sin, max_pos, T, H, D, rope_dim, rope_style, w, w_scale,
+                                        out, G, N, static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();
   return st;
 }

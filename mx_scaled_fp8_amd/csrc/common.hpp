@@ -38,6 +38,7 @@ enum Counter {
   C_BMM_BF16_LARGE,
   C_BMM_BF16_SMALL,
   C_EXPAND_SCALES,
+  C_WOA_FUSED,
 };
 void count(Counter c);
 

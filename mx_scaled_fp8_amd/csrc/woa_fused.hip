@@ -1,0 +1,500 @@
+// Single-kernel wo_a (gfx950): inverse RoPE, group-128 E8M0 quantisation and
+// the batched a8w8 MX-scale GEMM in one pass, the activation going from BF16
+// to FP8 inside the GEMM's A-tile load.
+//
+// "[ROCm][DSV4][Perf] Use FP8 WO_A output projection", Summary: the path is
+// an inverse RoPE fused with per-token E8M0 group quantisation, then the MX
+// batched GEMM with the checkpoint's FP8 weight.  The pages run the two as
+// separate operators; here the quantiser's output never leaves the compute
+// unit: out[t, g, n] = sum_k dec(q[t,g,k]) 2^(sa-127) dec(W[g,n,k]) 2^(sw-127)
+// with q, sa exactly the quantiser's (OCP codes; the result of an FNUZ run
+// is the same), fp32 accumulation, BF16 out.
+//
+// Design: the 256 (t) x 256 (n) tiles, 4 waves of 128 x 128 and
+// v_mfma_scale_f32_32x32x64_f8f6f4 of bmm_large_kernel, one tile per
+// workgroup, K-steps of 128.  A 128-wide K-step of a token row is exactly one
+// quantisation group, so each stage quantises whole groups:
+//  * A arrives as BF16 in registers: 8 lanes per token row, each lane two
+//    16-byte chunks (a, a + d) of the row's 256-byte stage slice, 8 rows per
+//    load instruction (two instructions per 8 rows, 16 per wave per stage);
+//  * a stage that holds the last 128 dims of a head rotates its last R dims
+//    (fp32, products and sums rounded one by one, BF16 nearest even): with
+//    d = 8 the interleaved pairs lie inside a chunk, with d = R/16 the
+//    split-half pairs (i, i + R/2) are the lane's two chunks;
+//  * the group amax is a packed-u16 max over the lane's 16 values and three
+//    DPP steps over the row's 8 lanes; the E8M0 byte is integer arithmetic on
+//    its bits; the codes come from v_cvt_scalef32_pk_fp8_bf16 (the
+//    quantiser's instructions, so the codes are the quantiser's);
+//  * codes go to the stage's A buffer in LDS (the swizzled layout the MFMA
+//    fragment reads use), scale bytes to a per-stage A-scale slot;
+//  * W goes global -> LDS by LDS-DMA as in bmm_large_kernel.
+// Per stage: the MFMAs of stage kb from LDS; meanwhile this wave quantises
+// stage kb+1 from its registers into the other buffer and loads stage kb+2's
+// BF16; one barrier; then the W DMA of stage kb+2 into the buffer stage kb
+// used.  A token whose position is outside the table gets NaN scales (its
+// outputs are NaN), as from the quantiser.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace mx {
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kTile = 256;                  // tile rows along t and n
+constexpr int kBK = 128;                    // K bytes of FP8 per stage = one quantisation group
+constexpr int kOpBytes = kTile * kBK;       // 32 KiB per operand per stage
+constexpr int kMaxKB = 32;                  // K <= 4096: the W scales of a tile stay in LDS
+constexpr int kFmtFp8 = 0;
+
+// vector-memory instructions a wave issues per stage (the waits below count them)
+constexpr int kALoadsPerStage = 16;         // 8 row groups x 2 chunks
+constexpr int kWDmaPerStage = kTile / 32;   // 8 row groups of 32 rows, one DMA instruction each
+
+// s_waitcnt immediate for vmcnt(n) with lgkmcnt(0) and expcnt left alone
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int kWaitVmMax = 0xC07F;          // vmcnt(63), lgkmcnt(0): LDS traffic only
+static_assert(wait_vm(16) == 0x4070 && wait_vm(8) == 0x0078 && wait_vm(0) == 0x0070, "waitcnt encoding");
+
+struct FusedArgs {
+  const uint16_t* x;          // [T, H*D] BF16
+  const int64_t* pos;         // [T]
+  const uint16_t* cos;        // [max_pos, R/2]
+  const uint16_t* sin;
+  int64_t max_pos;
+  const uint8_t* w;           // [G, N, K] OCP e4m3
+  const uint8_t* sw;          // [G, N, K/128]
+  uint16_t* out;              // [T, G, N]
+  int T, G, N, K, D, R;
+  int cd;                     // chunk distance of a lane's two chunks: 8, or R/16 (split halves)
+  int tiles_t, tiles_n, total_tiles, per_xcd;
+};
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) ^ ((r & 1) << 2)) & 7; }
+
+// Workgroup barrier that the compiler may not move memory accesses across
+// (the waits that make the data visible are issued explicitly before it).
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ v8i make_v8i(const uint4 lo, const uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// max over the 8 lanes of a row: xor 1, xor 2 (quad permutes), then lane i
+// against lane 7 - i (row_half_mirror) joins the two quads
+__device__ __forceinline__ uint32_t max8(uint32_t m) {
+  m = max(m, dpp<0xB1>(m));
+  m = max(m, dpp<0x4E>(m));
+  m = max(m, dpp<0x141>(m));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t amax_bits8(const uint4 v) {
+  const v2u16 a = __builtin_bit_cast(v2u16, v.x & 0x7FFF7FFFu);
+  const v2u16 b = __builtin_bit_cast(v2u16, v.y & 0x7FFF7FFFu);
+  const v2u16 c = __builtin_bit_cast(v2u16, v.z & 0x7FFF7FFFu);
+  const v2u16 d = __builtin_bit_cast(v2u16, v.w & 0x7FFF7FFFu);
+  const v2u16 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max(static_cast<uint32_t>(m[0]), static_cast<uint32_t>(m[1]));
+}
+
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  const v2bf r = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// (x, y) -> (x*c + y*s, y*c - x*s), every operation rounded to fp32
+__device__ __forceinline__ void inv_rotate(float x, float y, float c, float s, float& xr, float& yr) {
+  const float xc = x * c, ys = y * s, yc = y * c, xs = x * s;
+  xr = xc + ys;
+  yr = yc - xs;
+}
+
+// OCP codes of the 8 BF16 values of v divided by 2^e (sbits: E8M0 byte << 23)
+__device__ __forceinline__ uint2 encode8(const uint4 v, float sbits) {
+  v2s lo = {0, 0}, hi = {0, 0};
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.x), sbits, false);
+  lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.y), sbits, true);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(v2bf, v.z), sbits, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(v2bf, v.w), sbits, true);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// W tile I times A tile J; the scale operands are 4-byte words holding the
+// scales of tiles 0..3 and the byte selects pick tile I's and J's
+template <int I, int J>
+__device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+                                        uint32_t sav) {
+  acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[I], a[J], acc[I][J], kFmtFp8, kFmtFp8, I,
+                                                             static_cast<int>(swv), J, static_cast<int>(sav));
+}
+
+template <int IJ = 0>
+__device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+                                         uint32_t sav) {
+  if constexpr (IJ < 16) {
+    mfma_ij<IJ / 4, IJ % 4>(acc, w, a, swv, sav);
+    mfma_all<IJ + 1>(acc, w, a, swv, sav);
+  }
+}
+
+template <bool ROPE, bool NEOX>
+__global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
+  // stage buffers: [W tile 256 x 128 B | A tile 256 x 128 B]
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kOpBytes];
+  // W scales of every stage of the tile, [stage][wave half][row % 32][tile]
+  __shared__ __attribute__((aligned(16))) uint8_t wsc[kMaxKB][2][32][4];
+  // A scales of the stage in each buffer, [buffer][wave half][row % 32][tile]
+  __shared__ __attribute__((aligned(16))) uint8_t asc[2][2][32][4];
+  // positions of the tile's rows (-1: outside the table)
+  __shared__ int32_t spos[kTile];
+
+  const int xcd = blockIdx.x & 7;
+  const int work = xcd * p.per_xcd + (blockIdx.x >> 3);
+  if (work >= p.total_tiles) return;
+  const int nt = work % p.tiles_n;
+  const int tt = (work / p.tiles_n) % p.tiles_t;
+  const int g = work / (p.tiles_n * p.tiles_t);
+  const int t0 = tt * kTile, n0 = nt * kTile;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wt = wave >> 1;
+  const int KB = p.K / kBK;                        // <= kMaxKB
+  const int kb0 = (tt + nt) % KB;                  // K rotation, as bmm_large_kernel
+  const int L = p.G * p.K;                         // elements per token row (H * D)
+  auto real_stage = [&](int kb) {
+    int kr = kb + kb0;
+    return kr >= KB ? kr - KB : kr;
+  };
+
+  // ---- W: LDS-DMA of the stage's 256 rows (rows past N re-read the last one)
+  const int dma_row = wave * 8 + (lane >> 3);
+  const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz8(dma_row)) * 16;
+  const uint8_t* baseW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
+  const int limW = p.N - 1 - n0;
+  // lane offset of row group 0 and the cap past which rows re-read the last one
+  const uint32_t offW0 = static_cast<uint32_t>(dma_row) * static_cast<uint32_t>(p.K) + dma_chunk;
+  const uint32_t capW = static_cast<uint32_t>(limW) * static_cast<uint32_t>(p.K) + dma_chunk;
+  auto issue_w = [&](uint8_t* buf, int kb) {
+    const uint8_t* bW = baseW + static_cast<uint32_t>(real_stage(kb)) * kBK;
+#pragma unroll
+    for (int it = 0; it < kWDmaPerStage; ++it) {
+      uint32_t b = offW0;
+      asm volatile("" : "+v"(b));                    // formed per issue, not held as 8 addresses
+      const uint32_t o = min(b + static_cast<uint32_t>(it * 32) * static_cast<uint32_t>(p.K), capW);
+      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(buf + (it * 32 + wave * 8) * kBK), 16, 0, 0);
+    }
+  };
+
+  // ---- A: lane (row ri = lane / 8 of a group of 8 rows, c = lane % 8)
+  // holds chunks ca and ca + cd of the row's 16 chunks of 8 BF16; wave w
+  // owns tile rows 64w .. 64w + 63 (row group j: rows 64w + 8j + ri)
+  const int ri = lane >> 3, c = lane & 7;
+  const int cd = p.cd;
+  const int ca = (c / cd) * 2 * cd + (c % cd);
+  const int cb = ca + cd;
+  const int arow0 = wave * 64 + ri;               // tile row of row group 0
+  // the tile's first row, group g: a wave-uniform base; lanes add a 32-bit
+  // offset (row * row bytes + chunk), rows past T clamped to the last one
+  const uint8_t* xtile = reinterpret_cast<const uint8_t*>(p.x + static_cast<size_t>(t0) * L +
+                                                          static_cast<size_t>(g) * p.K);
+  const int limT = p.T - 1 - t0;
+  const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
+  uint4 av[8][2];
+  auto load_a = [&](int kb) {
+    const uint8_t* base = xtile + real_stage(kb) * (2 * kBK);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t r = static_cast<uint32_t>(min(arow0 + 8 * j, limT));
+      // formed here, not hoisted out of the loop as 8 live 64-bit addresses
+      asm volatile("" : "+v"(r));
+      const uint32_t o = r * row_bytes + static_cast<uint32_t>(ca) * 16;
+      av[j][0] = *reinterpret_cast<const uint4*>(base + o);
+      av[j][1] = *reinterpret_cast<const uint4*>(base + o + static_cast<uint32_t>(cd) * 16);
+    }
+  };
+
+  // rows of the lane's row groups whose position is outside the table (bit j)
+  uint32_t bad_rows = 0;
+  const int R = p.R;
+  const int half = R >> 1;
+  // is the stage at element offset `col` of group g the last 128 dims of a head?
+  auto rope_stage = [&](int kb) {
+    if constexpr (!ROPE) return false;
+    const int colg = g * p.K + real_stage(kb) * kBK;
+    return (colg + kBK) % p.D == 0;
+  };
+
+  // ---- quantise the stage in av[] into buffer `buf` (A region) and asc[sb]
+  // LDS byte offsets of the lane's two 8-byte code pieces in row group 0:
+  // row tr = arow0 + 8j is at + 1024 j, and its swizzle swz8(tr) depends on
+  // tr % 16 only, so it is swz8(ri) for even j and swz8(ri) ^ 4 for odd j
+  const int szr = swz8(ri);
+  auto piece_off = [&](int ch, int sz) { return (((ch >> 1) ^ sz) << 4) + (ch & 1) * 8; };
+  const uint32_t qoff[2][2] = {
+      {static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr)),
+       static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr ^ 4))},
+      {static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(cb, szr)),
+       static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(cb, szr ^ 4))}};
+  // asc byte of tile row tr = 64 wave + ri + 8j: [tr / 128][tr % 32][(tr / 32) % 4]
+  const int sc_lane = (wave >> 1) * 128 + ri * 4;
+  // rotate the rope stage's last R dims of every valid row, in place in av[]
+  auto rotate = [&]() {
+    const int first_rot = (kBK - R) / 8;           // first rotated chunk of the stage
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if ((bad_rows >> j) & 1) continue;
+      const int pj = spos[arow0 + 8 * j];
+      const uint16_t* crow = p.cos + static_cast<int64_t>(pj) * half;
+      const uint16_t* srow = p.sin + static_cast<int64_t>(pj) * half;
+      if constexpr (!NEOX) {
+        // pairs (2i, 2i+1) of the rotated slice: a chunk's 4 dwords are 4 pairs
+        auto rot_chunk = [&](uint4& v, int ch) {
+          if (ch < first_rot) return;
+          const int i0 = (ch - first_rot) * 4;
+          const uint2 cc = *reinterpret_cast<const uint2*>(crow + i0);
+          const uint2 ss = *reinterpret_cast<const uint2*>(srow + i0);
+          float xr, yr;
+          inv_rotate(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(cc.x), bf16_lo(ss.x), xr, yr);
+          v.x = pk_bf16(xr, yr);
+          inv_rotate(bf16_lo(v.y), bf16_hi(v.y), bf16_hi(cc.x), bf16_hi(ss.x), xr, yr);
+          v.y = pk_bf16(xr, yr);
+          inv_rotate(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(cc.y), bf16_lo(ss.y), xr, yr);
+          v.z = pk_bf16(xr, yr);
+          inv_rotate(bf16_lo(v.w), bf16_hi(v.w), bf16_hi(cc.y), bf16_hi(ss.y), xr, yr);
+          v.w = pk_bf16(xr, yr);
+        };
+        rot_chunk(av[j][0], ca);
+        rot_chunk(av[j][1], cb);
+      } else {
+        // pairs (i, i + R/2): chunk ca holds x of pairs i0 .. i0+7, chunk cb their y
+        if (ca >= first_rot) {
+          const int i0 = (ca - first_rot) * 8;
+          const uint4 cc = *reinterpret_cast<const uint4*>(crow + i0);
+          const uint4 ss = *reinterpret_cast<const uint4*>(srow + i0);
+          uint4& vx = av[j][0];
+          uint4& vy = av[j][1];
+          uint32_t xw[4] = {vx.x, vx.y, vx.z, vx.w};
+          uint32_t yw[4] = {vy.x, vy.y, vy.z, vy.w};
+          const uint32_t cw[4] = {cc.x, cc.y, cc.z, cc.w};
+          const uint32_t sw4[4] = {ss.x, ss.y, ss.z, ss.w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            float x0, y0, x1, y1;
+            inv_rotate(bf16_lo(xw[k]), bf16_lo(yw[k]), bf16_lo(cw[k]), bf16_lo(sw4[k]), x0, y0);
+            inv_rotate(bf16_hi(xw[k]), bf16_hi(yw[k]), bf16_hi(cw[k]), bf16_hi(sw4[k]), x1, y1);
+            xw[k] = pk_bf16(x0, x1);
+            yw[k] = pk_bf16(y0, y1);
+          }
+          vx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+          vy = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto quantise = [&](int kb, uint8_t* buf, int sb) {
+    if (ROPE && rope_stage(kb)) rotate();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 v0 = av[j][0], v1 = av[j][1];
+      uint32_t m = max(amax_bits8(v0), amax_bits8(v1));
+      if (ROPE && ((bad_rows >> j) & 1)) m = 0x7F80u;   // position outside the table: NaN scale
+      m = max8(m);
+      const bool finite = m < 0x7F80u;
+      const int e = e8m0_exponent<8>(finite ? m : 0);
+      const float sbits = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+      uint2 q0 = encode8(v0, sbits), q1 = encode8(v1, sbits);
+      if (!finite) q0 = q1 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+      uint32_t o0 = qoff[0][j & 1], o1 = qoff[1][j & 1];
+      asm volatile("" : "+v"(o0), "+v"(o1));        // not hoisted per row group
+      *reinterpret_cast<uint2*>(buf + o0 + j * 8 * kBK) = q0;
+      *reinterpret_cast<uint2*>(buf + o1 + j * 8 * kBK) = q1;
+      if (c == 0)
+        (&asc[sb][0][0][0])[sc_lane + (j & 3) * 32 + ((2 * wave + (j >> 2)) & 3)] =
+            static_cast<uint8_t>(finite ? e + 127 : 0xFF);
+      // one row group's temporaries at a time
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- fragments (as bmm_large_kernel): row wn*128 + 32i + lane%32 of W,
+  // wt*128 + 32j + lane%32 of A; lane group q2 takes logical chunks 4h + q2
+  // and 4h + q2 + 2 of 64-K half h
+  const int r32 = lane & 31;
+  const int q2 = lane >> 5;
+  const int rdW = (wn * 128 + r32) * kBK;
+  const int rdA = kOpBytes + (wt * 128 + r32) * kBK;
+  const int sz = swz8(r32);
+  const int ch0[2] = {(q2 ^ sz) << 4, ((4 + q2) ^ sz) << 4};
+  const int ch1[2] = {((q2 + 2) ^ sz) << 4, ((6 + q2) ^ sz) << 4};
+  auto read_frag = [&](const uint8_t* q, int h) {
+    return make_v8i(*reinterpret_cast<const uint4*>(q + ch0[h]), *reinterpret_cast<const uint4*>(q + ch1[h]));
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto mma_stage = [&](const uint8_t* buf, int kb, int sb) {
+    const uint32_t swv = *reinterpret_cast<const uint32_t*>(&wsc[real_stage(kb)][wn][r32][0]);
+    const uint32_t sav = *reinterpret_cast<const uint32_t*>(&asc[sb][wt][r32][0]);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // one half's fragments at a time (64 VGPRs): the BF16 of the next
+      // stage is held in registers meanwhile
+      __builtin_amdgcn_sched_barrier(0);
+      v8i fw[4], fa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fw[i] = read_frag(buf + rdW + i * 32 * kBK, h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fa[j] = read_frag(buf + rdA + j * 32 * kBK, h);
+      mfma_all(acc, fw, fa, swv, sav);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: positions, the tile's W scales, stage 0 quantised, stage 1 on its way
+  if constexpr (ROPE) {
+    const int64_t pp = p.pos[min(t0 + tid, p.T - 1)];
+    spos[tid] = (pp >= 0 && pp < p.max_pos) ? static_cast<int32_t>(pp) : -1;
+  }
+  {
+    // thread tid stages W row tid's scale bytes of all stages
+    const uint8_t* scw = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
+    for (int s = 0; s < KB; ++s) wsc[s][tid >> 7][tid & 31][(tid >> 5) & 3] = scw[s];
+  }
+  issue_w(st0, 0);
+  load_a(0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  stage_barrier();
+  if constexpr (ROPE) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bad_rows |= (spos[arow0 + 8 * j] < 0 ? 1u : 0u) << j;
+  }
+
+  // ---- stage loop.  On entry to iteration kb >= 0: buffer kb%2 holds stage
+  // kb (W and the quantised A); this wave's loads of stage kb+1's BF16 and
+  // then the DMA of its W (into the other buffer) may be in flight.
+  // Iteration -1 only quantises stage 0 (its loads have landed) and starts
+  // stage 1.
+  for (int kb = -1; kb < KB; ++kb) {
+    uint8_t* cur = (kb & 1) ? st1 : st0;
+    uint8_t* nxt = (kb & 1) ? st0 : st1;
+    if (kb >= 0) mma_stage(cur, kb, kb & 1);
+    if (kb + 1 < KB) {
+      // stage kb+1's BF16 has landed once at most its W DMA is pending (at
+      // kb = -1 nothing is)
+      __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
+      quantise(kb + 1, nxt, (kb + 1) & 1);
+      if (kb + 2 < KB) {
+        load_a(kb + 2);
+        if (kb < 0) issue_w(cur, kb + 2);         // stage 1's W: its buffer has not been used
+        // stage kb+1's W has landed once at most stage kb+2's loads are
+        // pending (at kb = -1 stage 0's W landed before the loop, and
+        // stage 1's DMA above may stay in flight)
+        if (kb >= 0)
+          __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
+        else
+          __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage + kWDmaPerStage));
+      } else {
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
+      }
+    }
+    stage_barrier();                                 // everyone is done with `cur`; stage kb+1 is in `nxt`
+    if (kb >= 0 && kb + 2 < KB) issue_w(cur, kb + 2);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));          // no DMA outlives the workgroup
+
+  // ---- epilogue straight from the accumulators (as bmm_large_kernel)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = t0 + wt * 128 + j * 32 + r32;
+    uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const v16f& v = acc[i][j];
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
+        const uint32_t y0 = pack_bf16x2(v[8 * pp + 4], v[8 * pp + 5]), y1 = pack_bf16x2(v[8 * pp + 6], v[8 * pp + 7]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        const int n = n0 + wn * 128 + i * 32 + pp * 16 + q2 * 8;
+        if (t < p.T && n < p.N) *reinterpret_cast<uint4*>(orow + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Fused wo_a dispatch (arguments validated by the caller: K % 128 == 0,
+// K <= 4096, D % 128 == 0, R <= 128 and R % 16 == 0 (R in {16, 32, 64, 128}
+// for split halves), N % 16 == 0, T >= 1).
+mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* cos, const void* sin,
+                           int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
+                           const uint8_t* w, const uint8_t* w_scale, void* out, int32_t G, int32_t N,
+                           hipStream_t stream) {
+  FusedArgs p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.pos = positions;
+  p.cos = static_cast<const uint16_t*>(cos);
+  p.sin = static_cast<const uint16_t*>(sin);
+  p.max_pos = max_pos;
+  p.w = w;
+  p.sw = w_scale;
+  p.out = static_cast<uint16_t*>(out);
+  p.T = static_cast<int>(T);
+  p.G = G;
+  p.N = N;
+  p.K = static_cast<int>(static_cast<int64_t>(H) * D / G);
+  p.D = D;
+  p.R = rope_dim;
+  const bool neox = style == MX_ROPE_NEOX && rope_dim > 0;
+  p.cd = neox ? rope_dim / 16 : 8;
+  p.tiles_t = static_cast<int>((T + kTile - 1) / kTile);
+  p.tiles_n = (N + kTile - 1) / kTile;
+  p.total_tiles = p.tiles_t * p.tiles_n * G;
+  p.per_xcd = (p.total_tiles + 7) / 8;
+  const int grid = p.per_xcd * 8;
+  if (rope_dim == 0)
+    woa_fused_kernel<false, false><<<grid, 256, 0, stream>>>(p);
+  else if (neox)
+    woa_fused_kernel<true, true><<<grid, 256, 0, stream>>>(p);
+  else
+    woa_fused_kernel<true, false><<<grid, 256, 0, stream>>>(p);
+  return launch_status("mx_wo_a_fused");
+}
+
+}  // namespace mx

@@ -10,6 +10,8 @@ kernel over all 512 tiles).
 * GEMM: every one of the 134,217,728 outputs within 2^-7 |ref| + 1e-3 rms(ref)
   of the unrounded fp64 oracle run on the oracle's own codes and scales, rms
   over the whole output.
+* The single-kernel wo_a (mx_wo_a_fused) on the same chunk: every output
+  within the same bound of the same reference.
 
 The oracle runs over the rows in threads (numpy releases the interpreter lock
 in its array loops); it is the same oracle, only scheduled over row blocks.
@@ -52,9 +54,10 @@ def chunk():
     q, s = mx.mx_inv_rope_group_quant(x, dev_i64(p.positions), dev_u16(cos), dev_u16(sin), p.H, p.D, 64)
     wd, swd = dev_u8(p.w), dev_u8(p.w_scale)
     out = mx.mx_bmm_a8w8_mxscale(q.view(p.T, p.G, p.K), s.view(p.T, p.G, -1), wd, swd)
+    fused = mx.mx_wo_a_fused(x, dev_i64(p.positions), dev_u16(cos), dev_u16(sin), p.H, p.D, 64, wd, swd)
     torch.cuda.synchronize()
-    gq, gs, gout = host_u8(q), host_u8(s), host_u16(out)
-    del q, s, out
+    gq, gs, gout, gfused = host_u8(q), host_u8(s), host_u16(out), host_u16(fused)
+    del q, s, out, fused
     say("full prefill chunk: oracle rotation over all rows")
     rot = np.concatenate(_rows_parallel(
         lambda a, b: inverse_rope(p.x[a:b], p.positions[a:b], cos, sin, p.H, p.D, 64), p.T))
@@ -62,7 +65,7 @@ def chunk():
     parts = _rows_parallel(lambda a, b: group_quant(rot[a:b], 128, F.OCP), p.T)
     rq = np.concatenate([a for a, _ in parts])
     rs = np.concatenate([b for _, b in parts])
-    return dict(p=p, x=x, wd=wd, swd=swd, gq=gq, gs=gs, gout=gout, rot=rot, rq=rq, rs=rs)
+    return dict(p=p, x=x, wd=wd, swd=swd, gq=gq, gs=gs, gout=gout, gfused=gfused, rot=rot, rq=rq, rs=rs)
 
 
 def test_fused_quantiser_every_row(chunk):
@@ -81,10 +84,23 @@ def test_quantiser_on_rotated_bf16_bit_exact(chunk):
                        what="prefill chunk from rotated BF16")
 
 
-def test_gemm_every_output(chunk):
+@pytest.fixture(scope="module")
+def gemm_ref(chunk):
     p = chunk["p"]
     say("full prefill chunk: fp64 oracle GEMM over every output")
-    ref = G.bmm_a8w8_mxscale(chunk["rq"].reshape(p.T, p.G, p.K), chunk["rs"].reshape(p.T, p.G, -1), p.w,
-                             p.w_scale)
-    worst = assert_gemm_close(chunk["gout"].reshape(p.T, p.G, p.N), ref, "prefill chunk, every output")
-    say(f"GEMM: worst |err| / bound = {worst:.3g} over {ref.size} outputs")
+    return G.bmm_a8w8_mxscale(chunk["rq"].reshape(p.T, p.G, p.K), chunk["rs"].reshape(p.T, p.G, -1), p.w,
+                              p.w_scale)
+
+
+def test_gemm_every_output(chunk, gemm_ref):
+    p = chunk["p"]
+    worst = assert_gemm_close(chunk["gout"].reshape(p.T, p.G, p.N), gemm_ref, "prefill chunk, every output")
+    say(f"GEMM: worst |err| / bound = {worst:.3g} over {gemm_ref.size} outputs")
+
+
+def test_single_kernel_wo_a_every_output(chunk, gemm_ref):
+    """mx_wo_a_fused over the same chunk: every output within the bound of
+    the oracle's quantise-then-GEMM result."""
+    p = chunk["p"]
+    worst = assert_gemm_close(chunk["gfused"].reshape(p.T, p.G, p.N), gemm_ref, "single-kernel wo_a, every output")
+    say(f"single-kernel wo_a: worst |err| / bound = {worst:.3g}")
