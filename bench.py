@@ -12,7 +12,8 @@ Printed: one JSON line -- the headline, with `roofline` for the GEMM
 (the CPU oracle timed on a bounded sample of the same workload) and `parity`
 (the timed run's codes, scales and outputs on that sample against the
 oracle's), then `secondary`: the decode batch, the MXFP8 linear at its four
-K and the 100,000-token chunked prefill (OCP and FNUZ), each with its
+K (64 rows, and 8192 rows at N = 5120) and the 100,000-token chunked
+prefill (OCP and FNUZ), each with its
 roofline fraction, the oracle's time and a parity record.  --extra adds the
 production down_proj, the load-time dequant and the BF16 arm.  Progress goes
 to stderr.  The exit status is 3 if any parity record fails.
@@ -162,8 +163,26 @@ def bench_prefill(mx, torch, workloads, steps, warmup, settle_ms, fmt=0):
     total_ms = e0.elapsed_time(e1)
     q_ms = np.array([a.elapsed_time(b) for a, b, _ in marks])
     b_ms = np.array([b.elapsed_time(c) for _, b, c in marks])
-    return dict(p=p, total_ms=total_ms, wall_s=wall, q_ms=q_ms, b_ms=b_ms, L=L, q=q, s=s, out=out,
-                settle={"ms": round(settle_wall_ms, 1), "steps": settle_steps, "requested_ms": settle_ms})
+    # the same step in one kernel (mx_wo_a_fused), right after, on the same
+    # resident chunk: `steps` launches, each timed
+    fout = torch.empty_like(out)
+    for _ in range(3):
+        mx.mx_wo_a_fused(x, pos, cosd, sind, p.H, p.D, 64, w, ws, out=fout)
+    fmarks = []
+    for _ in range(steps):
+        a = tm.event()
+        mx.mx_wo_a_fused(x, pos, cosd, sind, p.H, p.D, 64, w, ws, out=fout)
+        fmarks.append((a, tm.event()))
+    torch.cuda.synchronize()
+    f_ms = np.array([a.elapsed_time(b) for a, b in fmarks])
+    return dict(p=p, total_ms=total_ms, wall_s=wall, q_ms=q_ms, b_ms=b_ms, L=L, q=q, s=s, out=out, f_ms=f_ms,
+                fout=fout, settle={"ms": round(settle_wall_ms, 1), "steps": settle_steps, "requested_ms": settle_ms})
+
+
+def fused_bytes(T, G, N, K):
+    """Algorithmic HBM bytes of the one-kernel step: BF16 activations, W and
+    its scales, the positions and one cos/sin row per token, BF16 out."""
+    return T * G * K * 2 + G * N * K + G * N * K // 128 + T * (8 + 2 * 64) + T * G * N * 2
 
 
 def blas_threads():
@@ -394,6 +413,45 @@ def bench_linear(mx, torch, workloads, cpu, calls=40):
             rec["parity"] = parity_record(None, None, gout, None, None, ref, f"every output, K = {K}")
             rec["parity"]["f32_scales_to_e8m0_lossless"] = conv_ok
             rec["parity"]["pass"] = rec["parity"]["pass"] and conv_ok
+        res[f"K{K}"] = rec
+    return res
+
+
+def bench_linear_prefill(mx, torch, workloads, cpu, M=8192, N=5120):
+    """The MXFP8 linear at a prefill chunk's rows (M = 8192) and the pages'
+    production N = 5120, K in {288, 576, 1152, 2304}: per-call time (event
+    median), TFLOP/s against the branch's peak (BF16 for the dequantised
+    weight, FP8 for the block-scaled one), every output checked against the
+    oracle, and the oracle's time."""
+    dev = torch.device("cuda:0")
+    u16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    res = {}
+    for K in workloads.LINEAR_KS:
+        rng = np.random.default_rng(9000 + K)
+        xh = workloads.activations(rng, M, K)
+        wh = workloads.weight_codes(rng, (N, K))
+        wsh = workloads.scale_bytes(rng, (N, K // 32), -10, -4)
+        xd, wd, wsd = u16(xh), torch.from_numpy(wh).to(dev), torch.from_numpy(wsh).to(dev)
+        wprep = mx.mx_dequant_mxfp8_to_bf16(wd, wsd) if K % 128 else wd
+        o = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        wsp = torch.empty(max(1, mx.mx_linear_workspace_bytes(M, N, K, wprep.element_size())), dtype=torch.uint8,
+                          device=dev)
+        us, us_min = event_median_us(torch, lambda i: mx.mx_linear(xd, wprep, wsd, out=o, workspace=wsp), n=20)
+        flops = 2 * M * N * K
+        peak = PEAK_BF16_TFLOPS if K % 128 else PEAK_FP8_TFLOPS
+        rec = {"branch": "bf16 (dequantised at load)" if K % 128 else "block-scaled fp8 (x quantised per call)",
+               "us": us, "us_min": us_min, "TFLOPs": flops / us / 1e6,
+               "roofline": {"bound": "mfma", "peak": peak, "frac": flops / us / 1e6 / peak}}
+        torch.cuda.synchronize()
+        gout = o.view(torch.int16).cpu().numpy().view(np.uint16)
+        del xd, wd, wsd, wprep, o, wsp
+        if cpu:
+            from oracle.gemm import mx_linear as oracle_linear
+            with np.errstate(invalid="ignore"):
+                t0 = time.perf_counter()
+                ref = oracle_linear(xh, wh, wsh, 32)
+                rec["cpu_oracle_s"] = time.perf_counter() - t0
+            rec["parity"] = parity_record(None, None, gout, None, None, ref, f"every output, M = {M}, K = {K}")
         res[f"K{K}"] = rec
     return res
 
@@ -691,6 +749,19 @@ def main():
         "wall_s_timed_region": round(r["wall_s"], 4),
         "env": run_env(torch),
     }
+    f_avg_ms = float(r["f_ms"].mean())
+    fb = fused_bytes(p.T, p.G, p.N, p.K)
+    rec["single_kernel_wo_a"] = {
+        "kernel": "woa_fused_kernel", "launches": int(r["f_ms"].size), "us": round(f_avg_ms * 1e3, 2),
+        "us_min_median_max": [round(v, 1) for v in np.percentile(r["f_ms"] * 1e3, [0, 50, 100])],
+        "TFLOPs": round(p.flops / (f_avg_ms / 1e3) / 1e12, 1),
+        "frac_fp8_peak": round(p.flops / (f_avg_ms / 1e3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+        "algorithmic_bytes": fb, "two_kernel_algorithmic_bytes": qb + bmm_bytes(p.T, p.G, p.N, p.K),
+        "two_kernel_step_us": round(ms_step * 1e3, 2),
+        "step_speedup_vs_two_kernels": round(ms_step / f_avg_ms, 4),
+        "traffic": measured_traffic("woa_fused_kernel")}
+    log(f"[bench] single-kernel wo_a: {f_avg_ms * 1e3:.1f} us per launch against the {ms_step * 1e3:.1f} us "
+        f"two-kernel step")
     parity_ok = True
     if cpu:
         # the timed run's last results (every step computes the same values)
@@ -701,8 +772,11 @@ def main():
         rec["cpu_baseline"], rq, rs, ref = cpu_baseline(workloads, T)
         rec["parity"] = parity_record(gq, gs, gout, rq, rs, ref,
                                       f"timed run vs oracle, first {T} tokens (rms over those outputs)")
-        parity_ok &= rec["parity"]["pass"]
-        del gq, gs, gout, rq, rs, ref
+        gf = r["fout"][:T].view(torch.int16).cpu().numpy().view(np.uint16)
+        rec["single_kernel_wo_a"]["parity"] = parity_record(
+            None, None, gf, None, None, ref, f"single-kernel wo_a vs oracle, first {T} tokens")
+        parity_ok &= rec["parity"]["pass"] and rec["single_kernel_wo_a"]["parity"]["pass"]
+        del gq, gs, gout, gf, rq, rs, ref
     del r
     torch.cuda.empty_cache()
     if not args.no_secondary:
@@ -711,11 +785,15 @@ def main():
         log("[bench] MXFP8 linear")
         lin = bench_linear(mx, torch, workloads, cpu)
         torch.cuda.empty_cache()
+        log("[bench] MXFP8 linear, prefill rows")
+        linp = bench_linear_prefill(mx, torch, workloads, cpu)
+        torch.cuda.empty_cache()
         log("[bench] 100,000-token chunked prefill")
         lng = bench_long(mx, torch, workloads, cpu)
-        rec["secondary"] = {"decode_T64": dec, "mxfp8_linear_M64_N4096": lin, "long_prefill_100k": lng}
+        rec["secondary"] = {"decode_T64": dec, "mxfp8_linear_M64_N4096": lin, "mxfp8_linear_M8192_N5120": linp,
+                            "long_prefill_100k": lng}
         parities = [dec.get("parity"), *[v.get("parity") for v in lin.values()],
-                    lng["ocp"].get("parity"), lng["fnuz"].get("parity")]
+                    *[v.get("parity") for v in linp.values()], lng["ocp"].get("parity"), lng["fnuz"].get("parity")]
         parity_ok &= all(x["pass"] for x in parities if x is not None)
         parity_ok &= all(lng["fnuz_vs_ocp_last_chunk"].values())
         torch.cuda.empty_cache()

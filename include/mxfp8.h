@@ -169,11 +169,11 @@ mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t 
  * w        device u8 [G, N, K] OCP e4m3.   w_scale device u8 [G, N, K/128].
  * out      device BF16 [T, G, N].
  * Requires: T >= 0 (0 is a no-op), G >= 1, H*D % G == 0, K % 128 == 0,
- * K <= 4096, D % 128 == 0, rope_dim % 16 == 0 and rope_dim <= min(D, 128)
- * (split halves: rope_dim in {16, 32, 64, 128}), N >= 1 with N % 16 == 0,
- * x, w and out 16-byte aligned, positions 8-byte aligned, cos/sin 8-byte
- * aligned (16 for split halves), max_pos >= 1 when rope_dim > 0.  Other
- * shapes return MX_ERR_UNSUPPORTED (the two calls serve them).
+ * K <= 4096, D % 128 == 0, rope_dim % 16 == 0 and rope_dim <= min(D, 64)
+ * (split halves: rope_dim in {16, 32, 64}), N >= 1 with N % 16 == 0,
+ * x, w, out, cos and sin 16-byte aligned, positions 8-byte aligned,
+ * max_pos >= 1 when rope_dim > 0.  Other shapes return MX_ERR_UNSUPPORTED
+ * (the two calls serve them).
  */
 mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos,
                         const void* sin, int64_t max_pos, int64_t T, int32_t H, int32_t D,

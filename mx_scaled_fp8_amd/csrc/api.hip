@@ -246,7 +246,7 @@ mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos
   MX_CHECK(rope_style == MX_ROPE_INTERLEAVED || rope_style == MX_ROPE_NEOX, "%s: unknown rope style %d", fn,
            rope_style);
   // shapes the one-kernel path does not take: the two calls serve them
-  if (K > 4096 || D % 128 != 0 || rope_dim > 128 ||
+  if (K > 4096 || D % 128 != 0 || rope_dim > 64 ||
       (rope_style == MX_ROPE_NEOX && rope_dim > 0 && (rope_dim & (rope_dim - 1)) != 0))
     return fail(MX_ERR_UNSUPPORTED,
                 "%s: K = %lld, D = %d, rope_dim = %d (style %d) not served in one kernel; use "
@@ -258,9 +258,9 @@ mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos
   if (rope_dim > 0) {
     MX_CHECK(positions && cos && sin, "%s: rope_dim > 0 needs positions, cos and sin", fn);
     MX_CHECK(max_pos >= 1, "%s: max_pos = %lld", fn, (long long)max_pos);
-    const uintptr_t ta = rope_style == MX_ROPE_NEOX ? 16 : 8;
-    MX_CHECK(aligned(cos, ta) && aligned(sin, ta) && aligned(positions, 8),
-             "%s: cos/sin must be %d-byte aligned, positions 8-byte aligned", fn, (int)ta);
+    // the table rows are read in 16-byte pieces
+    MX_CHECK(aligned(cos, 16) && aligned(sin, 16) && aligned(positions, 8),
+             "%s: cos/sin must be 16-byte aligned, positions 8-byte aligned", fn);
   }
   MX_PREAMBLE();
   count(C_WOA_FUSED);

@@ -18,9 +18,11 @@
 //    16-byte chunks (a, a + d) of the row's 256-byte stage slice, 8 rows per
 //    load instruction (two instructions per 8 rows, 16 per wave per stage);
 //  * a stage that holds the last 128 dims of a head rotates its last R dims
-//    (fp32, products and sums rounded one by one, BF16 nearest even): with
-//    d = 8 the interleaved pairs lie inside a chunk, with d = R/16 the
-//    split-half pairs (i, i + R/2) are the lane's two chunks;
+//    (R <= 64; fp32, products and sums rounded one by one, BF16 nearest
+//    even): with d = 8 the interleaved pairs lie inside a chunk, with
+//    d = R/16 the split-half pairs (i, i + R/2) are the lane's two chunks;
+//    the tokens' cos/sin rows come by LDS-DMA into the stage's A buffer,
+//    each where its token's codes will go;
 //  * the group amax is a packed-u16 max over the lane's 16 values and three
 //    DPP steps over the row's 8 lanes; the E8M0 byte is integer arithmetic on
 //    its bits; the codes come from v_cvt_scalef32_pk_fp8_bf16 (the
@@ -34,6 +36,7 @@
 // used.  A token whose position is outside the table gets NaN scales (its
 // outputs are NaN), as from the quantiser.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -263,67 +266,97 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
        static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(cb, szr ^ 4))}};
   // asc byte of tile row tr = 64 wave + ri + 8j: [tr / 128][tr % 32][(tr / 32) % 4]
   const int sc_lane = (wave >> 1) * 128 + ri * 4;
-  // rotate the rope stage's last R dims of every valid row, in place in av[]
-  auto rotate = [&]() {
-    const int first_rot = (kBK - R) / 8;           // first rotated chunk of the stage
+  // ---- rotation tables of a rope stage: the cos and sin rows of the tile's
+  // tokens go by LDS-DMA into the A region of the stage's buffer (free until
+  // the stage's codes are written there), each at the 128 bytes its token's
+  // codes will take: cos[R/2] then sin[R/2] (R <= 64).  A wave loads and
+  // reads only its own 64 rows, and a row's codes are written after its
+  // rotation has read its tables, so no barrier is involved.  8 DMA
+  // instructions per wave: 8 lanes (16-byte pieces) per row, 8 rows each;
+  // pieces past the 2R bytes re-read the first (never used).
+  auto issue_cs = [&](uint8_t* buf, int kb) {
+    if (!ROPE || !rope_stage(kb)) return;
+    uint8_t* dst = buf + kOpBytes + wave * 64 * kBK;
+    const int piece = lane & 7;
+    const int npc = R >> 4;                          // 16-byte pieces per table row
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if ((bad_rows >> j) & 1) continue;
-      const int pj = spos[arow0 + 8 * j];
-      const uint16_t* crow = p.cos + static_cast<int64_t>(pj) * half;
-      const uint16_t* srow = p.sin + static_cast<int64_t>(pj) * half;
-      if constexpr (!NEOX) {
-        // pairs (2i, 2i+1) of the rotated slice: a chunk's 4 dwords are 4 pairs
-        auto rot_chunk = [&](uint4& v, int ch) {
-          if (ch < first_rot) return;
-          const int i0 = (ch - first_rot) * 4;
-          const uint2 cc = *reinterpret_cast<const uint2*>(crow + i0);
-          const uint2 ss = *reinterpret_cast<const uint2*>(srow + i0);
-          float xr, yr;
-          inv_rotate(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(cc.x), bf16_lo(ss.x), xr, yr);
-          v.x = pk_bf16(xr, yr);
-          inv_rotate(bf16_lo(v.y), bf16_hi(v.y), bf16_hi(cc.x), bf16_hi(ss.x), xr, yr);
-          v.y = pk_bf16(xr, yr);
-          inv_rotate(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(cc.y), bf16_lo(ss.y), xr, yr);
-          v.z = pk_bf16(xr, yr);
-          inv_rotate(bf16_lo(v.w), bf16_hi(v.w), bf16_hi(cc.y), bf16_hi(ss.y), xr, yr);
-          v.w = pk_bf16(xr, yr);
-        };
-        rot_chunk(av[j][0], ca);
-        rot_chunk(av[j][1], cb);
-      } else {
-        // pairs (i, i + R/2): chunk ca holds x of pairs i0 .. i0+7, chunk cb their y
-        if (ca >= first_rot) {
-          const int i0 = (ca - first_rot) * 8;
-          const uint4 cc = *reinterpret_cast<const uint4*>(crow + i0);
-          const uint4 ss = *reinterpret_cast<const uint4*>(srow + i0);
-          uint4& vx = av[j][0];
-          uint4& vy = av[j][1];
-          uint32_t xw[4] = {vx.x, vx.y, vx.z, vx.w};
-          uint32_t yw[4] = {vy.x, vy.y, vy.z, vy.w};
-          const uint32_t cw[4] = {cc.x, cc.y, cc.z, cc.w};
-          const uint32_t sw4[4] = {ss.x, ss.y, ss.z, ss.w};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            float x0, y0, x1, y1;
-            inv_rotate(bf16_lo(xw[k]), bf16_lo(yw[k]), bf16_lo(cw[k]), bf16_lo(sw4[k]), x0, y0);
-            inv_rotate(bf16_hi(xw[k]), bf16_hi(yw[k]), bf16_hi(cw[k]), bf16_hi(sw4[k]), x1, y1);
-            xw[k] = pk_bf16(x0, x1);
-            yw[k] = pk_bf16(y0, y1);
-          }
-          vx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-          vy = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < 8; ++k) {
+      int tr = wave * 64 + k * 8 + (lane >> 3);      // tile row
+      asm volatile("" : "+v"(tr));                   // read here, not hoisted as 8 live positions and pointers
+      const int pj = max(spos[tr], 0);               // outside the table: row 0 (its codes are NaN)
+      const uint16_t* src = piece < npc ? p.cos + static_cast<int64_t>(pj) * half + piece * 8
+                          : piece < 2 * npc ? p.sin + static_cast<int64_t>(pj) * half + (piece - npc) * 8
+                                            : p.cos + static_cast<int64_t>(pj) * half;
+      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + k * 1024), 16, 0, 0);
     }
   };
 
-  auto quantise = [&](int kb, uint8_t* buf, int sb) {
-    if (ROPE && rope_stage(kb)) rotate();
+  // rotation of one row group's two chunks (local copies), from the tables
+  // at `tab`: a chunk outside the rotated slice reads pair 0 and keeps its
+  // own value
+  const int first_rot = (kBK - R) / 8;             // first rotated chunk of a head's last stage
+  const bool rot_a = ca >= first_rot;
+  const bool rot_b = NEOX ? ca >= first_rot : cb >= first_rot;
+  const int ti_a = NEOX ? (rot_a ? (ca - first_rot) * 8 : 0) : (rot_a ? (ca - first_rot) * 4 : 0);
+  const int ti_b = NEOX ? ti_a : (rot_b ? (cb - first_rot) * 4 : 0);
+  auto rotate2 = [&](const uint8_t* tab, uint4& v0, uint4& v1) {
+    const uint16_t* crow = reinterpret_cast<const uint16_t*>(tab);
+    const uint16_t* srow = crow + half;
+    if constexpr (!NEOX) {
+      // pairs (2i, 2i+1) of the rotated slice: a chunk's 4 dwords are 4 pairs
+      auto rot_chunk = [&](const uint4 v, const uint2 cc, const uint2 ss) {
+        float xr, yr;
+        uint4 r;
+        inv_rotate(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(cc.x), bf16_lo(ss.x), xr, yr);
+        r.x = pk_bf16(xr, yr);
+        inv_rotate(bf16_lo(v.y), bf16_hi(v.y), bf16_hi(cc.x), bf16_hi(ss.x), xr, yr);
+        r.y = pk_bf16(xr, yr);
+        inv_rotate(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(cc.y), bf16_lo(ss.y), xr, yr);
+        r.z = pk_bf16(xr, yr);
+        inv_rotate(bf16_lo(v.w), bf16_hi(v.w), bf16_hi(cc.y), bf16_hi(ss.y), xr, yr);
+        r.w = pk_bf16(xr, yr);
+        return r;
+      };
+      const uint4 ra = rot_chunk(v0, *reinterpret_cast<const uint2*>(crow + ti_a),
+                                 *reinterpret_cast<const uint2*>(srow + ti_a));
+      const uint4 rb = rot_chunk(v1, *reinterpret_cast<const uint2*>(crow + ti_b),
+                                 *reinterpret_cast<const uint2*>(srow + ti_b));
+      if (rot_a) v0 = ra;
+      if (rot_b) v1 = rb;
+    } else {
+      // pairs (i, i + R/2): chunk ca holds x of pairs i0 .. i0+7, chunk cb their y
+      const uint4 cc = *reinterpret_cast<const uint4*>(crow + ti_a);
+      const uint4 ss = *reinterpret_cast<const uint4*>(srow + ti_a);
+      const uint32_t xw[4] = {v0.x, v0.y, v0.z, v0.w};
+      const uint32_t yw[4] = {v1.x, v1.y, v1.z, v1.w};
+      const uint32_t cw[4] = {cc.x, cc.y, cc.z, cc.w};
+      const uint32_t sw4[4] = {ss.x, ss.y, ss.z, ss.w};
+      uint32_t xo[4], yo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float x0, y0, x1, y1;
+        inv_rotate(bf16_lo(xw[k]), bf16_lo(yw[k]), bf16_lo(cw[k]), bf16_lo(sw4[k]), x0, y0);
+        inv_rotate(bf16_hi(xw[k]), bf16_hi(yw[k]), bf16_hi(cw[k]), bf16_hi(sw4[k]), x1, y1);
+        xo[k] = pk_bf16(x0, x1);
+        yo[k] = pk_bf16(y0, y1);
+      }
+      if (rot_a) {
+        v0 = make_uint4(xo[0], xo[1], xo[2], xo[3]);
+        v1 = make_uint4(yo[0], yo[1], yo[2], yo[3]);
+      }
+    }
+  };
+
+  // quantise stage kb from av[]: `rot` rotates it first (a rope stage); the
+  // two versions are separate code, chosen per stage, so that the rotation's
+  // registers are needed only in the stages that rotate
+  auto quantise_v = [&](auto rot, uint8_t* buf, int sb) {
+    constexpr bool RS = decltype(rot)::value;
+    const uint8_t* tab = buf + kOpBytes + arow0 * kBK;   // row group 0's tables (rope stage)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint4 v0 = av[j][0], v1 = av[j][1];
+      uint4 v0 = av[j][0], v1 = av[j][1];
+      if constexpr (RS) rotate2(tab + j * 8 * kBK, v0, v1);
       uint32_t m = max(amax_bits8(v0), amax_bits8(v1));
       if (ROPE && ((bad_rows >> j) & 1)) m = 0x7F80u;   // position outside the table: NaN scale
       m = max8(m);
@@ -342,6 +375,12 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
       // one row group's temporaries at a time
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  auto quantise = [&](int kb, uint8_t* buf, int sb) {
+    if (ROPE && rope_stage(kb))
+      quantise_v(std::true_type{}, buf, sb);
+    else
+      quantise_v(std::false_type{}, buf, sb);
   };
 
   // ---- fragments (as bmm_large_kernel): row wn*128 + 32i + lane%32 of W,
@@ -380,6 +419,12 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) fa[j] = read_frag(buf + rdA + j * 32 * kBK, h);
       mfma_all(acc, fw, fa, swv, sav);
+      // the MFMAs are pure: without a use here the compiler sinks them below
+      // the quantisation that follows, keeping their fragments live across it
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -394,14 +439,17 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     const uint8_t* scw = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
     for (int s = 0; s < KB; ++s) wsc[s][tid >> 7][tid & 31][(tid >> 5) & 3] = scw[s];
   }
-  issue_w(st0, 0);
-  load_a(0);
-  __builtin_amdgcn_s_waitcnt(wait_vm(0));
-  stage_barrier();
+  __builtin_amdgcn_s_waitcnt(kWaitVmMax);
+  stage_barrier();                                   // spos is written
   if constexpr (ROPE) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) bad_rows |= (spos[arow0 + 8 * j] < 0 ? 1u : 0u) << j;
   }
+  load_a(0);
+  issue_cs(st0, 0);
+  issue_w(st0, 0);
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  stage_barrier();
 
   // ---- stage loop.  On entry to iteration kb >= 0: buffer kb%2 holds stage
   // kb (W and the quantised A); this wave's loads of stage kb+1's BF16 and
@@ -411,28 +459,36 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   for (int kb = -1; kb < KB; ++kb) {
     uint8_t* cur = (kb & 1) ? st1 : st0;
     uint8_t* nxt = (kb & 1) ? st0 : st1;
+    if (kb + 1 < KB) {
+      // stage kb+1's BF16 (and rotation tables) have landed once at most its
+      // W DMA is pending (at kb = -1 nothing is)
+      __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
+    }
     if (kb >= 0) mma_stage(cur, kb, kb & 1);
     if (kb + 1 < KB) {
-      // stage kb+1's BF16 has landed once at most its W DMA is pending (at
-      // kb = -1 nothing is)
-      __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
       quantise(kb + 1, nxt, (kb + 1) & 1);
       if (kb + 2 < KB) {
         load_a(kb + 2);
-        if (kb < 0) issue_w(cur, kb + 2);         // stage 1's W: its buffer has not been used
+        if (kb < 0) {                             // stage 1: its buffer has not been used
+          issue_cs(cur, kb + 2);
+          issue_w(cur, kb + 2);
+        }
         // stage kb+1's W has landed once at most stage kb+2's loads are
         // pending (at kb = -1 stage 0's W landed before the loop, and
         // stage 1's DMA above may stay in flight)
         if (kb >= 0)
           __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
         else
-          __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage + kWDmaPerStage));
+          __builtin_amdgcn_s_waitcnt(kWaitVmMax);
       } else {
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
       }
     }
     stage_barrier();                                 // everyone is done with `cur`; stage kb+1 is in `nxt`
-    if (kb >= 0 && kb + 2 < KB) issue_w(cur, kb + 2);
+    if (kb >= 0 && kb + 2 < KB) {
+      issue_cs(cur, kb + 2);
+      issue_w(cur, kb + 2);
+    }
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));          // no DMA outlives the workgroup
 
@@ -443,7 +499,11 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const v16f& v = acc[i][j];
+      // the block's 16 values, each read out of its AGPR here (as plain
+      // reads the allocator moved accumulators into VGPRs and spilled)
+      float v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[k]) : "a"(acc[i][j][k]));
 #pragma unroll
       for (int pp = 0; pp < 2; ++pp) {
         const uint32_t x0 = pack_bf16x2(v[8 * pp + 0], v[8 * pp + 1]), x1 = pack_bf16x2(v[8 * pp + 2], v[8 * pp + 3]);
@@ -453,6 +513,8 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
         const int n = n0 + wn * 128 + i * 32 + pp * 16 + q2 * 8;
         if (t < p.T && n < p.N) *reinterpret_cast<uint4*>(orow + n) = make_uint4(s0[0], s1[0], s0[1], s1[1]);
       }
+      // one accumulator block at a time: read out of the AGPRs as it is stored
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
@@ -460,8 +522,8 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
 }  // namespace
 
 // Fused wo_a dispatch (arguments validated by the caller: K % 128 == 0,
-// K <= 4096, D % 128 == 0, R <= 128 and R % 16 == 0 (R in {16, 32, 64, 128}
-// for split halves), N % 16 == 0, T >= 1).
+// K <= 4096, D % 128 == 0, R <= 64 and R % 16 == 0 (R in {16, 32, 64} for
+// split halves), N % 16 == 0, T >= 1).
 mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* cos, const void* sin,
                            int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
                            const uint8_t* w, const uint8_t* w_scale, void* out, int32_t G, int32_t N,

@@ -52,7 +52,7 @@ def test_tiny(style):
 SHAPES = [
     (1, 1, 16, 1, 128, 64, INTERLEAVED),          # one stage, one row
     (17, 2, 272, 4, 128, 16, NEOX),                # ragged N tile, K = 256
-    (255, 3, 256, 6, 256, 128, INTERLEAVED),       # K = 512, rope over the whole last stage
+    (255, 3, 256, 6, 256, 48, INTERLEAVED),        # K = 512, 48 rotated dims (not a power of two)
     (256, 1, 512, 3, 128, 32, NEOX),               # exactly one t-tile, K = 384 (odd stage count)
     (257, 2, 528, 8, 256, 64, NEOX),               # one row past a t-tile, N past two tiles
     (300, 1, 64, 8, 512, 0, INTERLEAVED),          # no rotation, K = 4096
@@ -118,6 +118,9 @@ def test_declined_shapes_and_empty():
     s2 = torch.zeros((2, 16, 32), dtype=torch.uint8, device="cuda")
     with pytest.raises(mx.MxError, match="MX_ERR_UNSUPPORTED"):            # split halves of 48 dims
         mx.mx_wo_a_fused(x, pos, cs48, cs48, 16, 512, 48, w2, s2, mx.MX_ROPE_NEOX)
+    cs128 = torch.zeros((16, 64), dtype=torch.int16, device="cuda")
+    with pytest.raises(mx.MxError, match="MX_ERR_UNSUPPORTED"):            # more than 64 rotated dims
+        mx.mx_wo_a_fused(x, pos, cs128, cs128, 16, 512, 128, w2, s2)
     e = mx.mx_wo_a_fused(x[:0], pos[:0], cs, cs, 16, 512, 64, w2, s2)
     assert e.shape == (0, 2, 16)
     assert mx.mx_get_counters()["wo_a_fused"] == 0
