@@ -97,6 +97,13 @@ constexpr int kLN = 256;                 // tile rows along n
 constexpr int kBK = 128;                 // K bytes per stage = one scale group
 constexpr int kOpBytes = kLT * kBK;      // 32 KiB per operand per stage
 constexpr int kScaleWin = 32;            // stages whose scales are staged in LDS at once
+// LDS-DMA instructions a wave issues per stage: rows are moved 8 per
+// instruction per wave (32 per row group over the 4 waves), for both operands
+constexpr int kLargeDmaPerStage = 2 * (kLT / 32);
+static_assert(kLT == kLN && kLargeDmaPerStage == 16, "DMA instructions per stage");
+// stores a wave issues in the persistent kernel's folded epilogue: 8 chunks
+// of 32 rows, each leaving as 4 instructions of 8 rows x 128 bytes
+constexpr int kFoldStores = 8 * 4;
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
@@ -338,12 +345,14 @@ __global__ __launch_bounds__(256, 1) void bmm_large_kernel(LargeArgs p) {
       for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
   };
 
-  // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4,
-  // lgkmcnt 11:8).  The builtin, unlike inline asm, is seen by the compiler's
-  // own wait insertion, so it does not add a second, later drain.
-  constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
-  constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
-  constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
+  // s_waitcnt immediates, from the instruction counts they stand for.  The
+  // builtin, unlike inline asm, is seen by the compiler's own wait
+  // insertion, so it does not add a second, later drain.
+  constexpr int kWaitAll = wait_vm(0);
+  // the prologue leaves stage 1's DMA in flight: issue() is kLT / 32 row
+  // groups x 2 operands = kLargeDmaPerStage instructions per wave
+  constexpr int kWaitNewest16 = wait_vm(kLargeDmaPerStage);
+  constexpr int kWaitLgkm = kWaitLgkmOnly;
 
   // One stage, one barrier, in two parts.  On entry to front(kb) the first
   // 64-K half of stage kb is in registers (fw[0], fa[0]) with its scales,
@@ -679,10 +688,13 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
   };
-  constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
-  constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
-  constexpr int kWaitLgkm = 0xC07F;              // lgkmcnt(0)
-  constexpr int kWaitOlder32 = 0x8070;           // vmcnt(32) lgkmcnt(0)
+  constexpr int kWaitAll = wait_vm(0);
+  // the prologue leaves stage 1's DMA (kLargeDmaPerStage instructions) in flight
+  constexpr int kWaitNewest16 = wait_vm(kLargeDmaPerStage);
+  constexpr int kWaitLgkm = kWaitLgkmOnly;
+  // front_fold of an interior tile issues kFoldStores stores after the DMA
+  // of the next tile's stage 1; they may stay in flight
+  constexpr int kWaitOlder32 = wait_vm(kFoldStores);
 
   // front / back: the two halves of a stage, as in bmm_large_kernel.  back()
   // fetches stage `dma_kb` of the DMA tile into `cur` and reads the scales of
@@ -1088,7 +1100,7 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
     load(kt + 3 * W, 1);
   }
   if (kt < KB) compute(kt, 0);                // a last single step (buffer 0 holds it)
-  __builtin_amdgcn_s_waitcnt(0x0070);         // the clamped prefetches end here too
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));     // the clamped prefetches end here too
 
   // reduce over the waves in two rounds through 4 slots: waves 4..7 hand
   // their sums to waves 0..3, which then meet in the slots
@@ -1237,8 +1249,12 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   v4f acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  constexpr int kWaitStage = 0x4078;                 // vmcnt(24) lgkmcnt(0): 4 instructions x (kDecR - 2) stages
-  static_assert(4 * (kDecR - 2) == 24, "wait count");
+  // a stage is kDecDmaPerStage instructions per wave (issue(): 2 row groups x
+  // 2 operands); at the wait for stage kt, stages kt+1 .. kt+kDecR-2 may be
+  // in flight (the scale DMA is older than all of them)
+  constexpr int kDecDmaPerStage = 2 * 2;
+  constexpr int kWaitStage = wait_vm(kDecDmaPerStage * (kDecR - 2));
+  static_assert(kWaitStage == 0x4078, "vmcnt(24)");
 
 #pragma unroll 1
   for (int kt0 = 0; kt0 < KB; kt0 += kDecR) {
@@ -1278,7 +1294,7 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));           // no DMA outlives the workgroup
 
   // ---- C layout: lane l holds column l%16 (a token) and rows 4(l/16)..+3 (n)
 #pragma unroll
@@ -1370,8 +1386,14 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
   const uint8_t* sclW = scl + (lane & 15) * SPK + q;
   const uint8_t* sclA = scl + (kLinRowsW + 16 * wave + (lane & 15)) * SPK + q;
   v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
-  constexpr int kWaitStage = 0x4072;                 // vmcnt(18) lgkmcnt(0): 3 instructions x (kLinR - 2) stages
-  static_assert(3 * (kLinR - 2) == 18, "wait count");
+  // a stage is kLinDmaPerWave instructions per wave (issue(): ii = wave,
+  // wave + 4, wave + 8 of the (kLinRows + 16) / 8 = 12 row groups); at the
+  // wait for stage kt, stages kt+1 .. kt+kLinR-2 may be in flight (the scale
+  // DMA is older than all of them)
+  constexpr int kLinDmaPerWave = 3;
+  static_assert(4 * kLinDmaPerWave * 8 == kLinRows + 16, "row groups per stage");
+  constexpr int kWaitStage = wait_vm(kLinDmaPerWave * (kLinR - 2));
+  static_assert(kWaitStage == 0x4072, "vmcnt(18)");
 
   // (the compiler drains the DMA once per pass of this loop, at its head:
   // it cannot tell which slot the DMA pending there writes)
@@ -1392,7 +1414,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_dma_kernel(SmallArgs p) {
       acc = mfma_scaled(fw, fa, acc, sclW[4 * kt], sclA[4 * kt]);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);               // no DMA outlives the workgroup
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));           // no DMA outlives the workgroup
 
   const int t = 16 * wave + (lane & 15);
   const int n = n0 + 4 * q;

@@ -196,8 +196,11 @@ __global__ __launch_bounds__(256, 1) void bmm_bf16_persistent_kernel(Bf16Args p)
 #pragma unroll
       for (int j = 0; j < 4; ++j) asm volatile("" ::"a"(acc[i][j]));
   };
-  constexpr int kWaitAll = 0x0070;               // vmcnt(0) lgkmcnt(0)
-  constexpr int kWaitNewest16 = 0x4070;          // vmcnt(16) lgkmcnt(0)
+  constexpr int kWaitAll = wait_vm(0);
+  // the prologue leaves stage 1's DMA in flight: issue() is 8 row groups x 2
+  // operands per wave
+  constexpr int kWaitNewest16 = wait_vm(2 * (kTile / 32));
+  static_assert(2 * (kTile / 32) == 16, "DMA instructions per stage");
 
   // front: MFMAs of a stage's first 64 bytes (32 of them) while its second
   // half is read from `cur`; then wait for everything and barrier.

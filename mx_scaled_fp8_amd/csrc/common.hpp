@@ -67,6 +67,17 @@ inline DivU32 make_div(uint32_t d) {
 
 // ---------------------------------------------------------------- device side
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// bits 6:4, lgkmcnt bits 11:8).  wait_vm(n): at most n vector-memory
+// instructions of this wave outstanding (they complete in issue order: loads,
+// LDS-DMA and stores alike) and no LDS/scalar-memory instruction; expcnt is
+// not waited on.  kWaitLgkmOnly: LDS/scalar memory only.
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
+constexpr int kWaitLgkmOnly = wait_vm(63) | 0xF;
+static_assert(wait_vm(0) == 0x0070 && wait_vm(16) == 0x4070 && wait_vm(18) == 0x4072 && wait_vm(24) == 0x4078 &&
+                  wait_vm(32) == 0x8070 && kWaitLgkmOnly == 0xC07F,
+              "s_waitcnt encoding");
+
 __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 dv) {
   return dv.magic == 0 ? n : static_cast<uint32_t>(__umul64hi(static_cast<uint64_t>(n), dv.magic));
 }

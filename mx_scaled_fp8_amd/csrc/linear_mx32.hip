@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256, 1) void gemm_mx32_wres_kernel(WresArgs p) {
   }
 
   dma_weight_slice(p.w, p.sw, n0, p.K, sW, sS, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0x0070);          // vmcnt(0) lgkmcnt(0): this wave's loads have landed
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));      // this wave's loads have landed
   __builtin_amdgcn_s_barrier();                // and every wave's
 
   const v4f acc = mfma_steps<SPW, TT == 1>(sW, sS, p.K, kb0, lane, xf, xsb);
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, 1) void linear_mx32_fused_kernel(FusedArgs p) 
     const auto t32 = __builtin_amdgcn_permlane32_swap(t16[0], t16[1], false, false);
     xsb[j] = static_cast<int>(q == 0 ? s1 : q == 3 ? s2 : q == 1 ? (t32[1] & 0xFFu) : ((t32[0] >> 8) & 0xFFu));
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);          // vmcnt(0) lgkmcnt(0): this wave's loads have landed
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));      // this wave's loads have landed
   __builtin_amdgcn_s_barrier();                // and every wave's
 
   const v4f acc = mfma_steps<SPW, true>(sW, sS, p.K, kb0, lane, xf, xsb);

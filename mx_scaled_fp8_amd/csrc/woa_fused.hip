@@ -61,11 +61,8 @@ constexpr int kFmtFp8 = 0;
 constexpr int kALoadsPerStage = 16;         // 8 row groups x 2 chunks
 constexpr int kWDmaPerStage = kTile / 32;   // 8 row groups of 32 rows, one DMA instruction each
 
-// s_waitcnt immediate for vmcnt(n) with lgkmcnt(0) and expcnt left alone
-// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
-constexpr int kWaitVmMax = 0xC07F;          // vmcnt(63), lgkmcnt(0): LDS traffic only
-static_assert(wait_vm(16) == 0x4070 && wait_vm(8) == 0x0078 && wait_vm(0) == 0x0070, "waitcnt encoding");
+constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
+static_assert(kALoadsPerStage == 8 * 2 && kWDmaPerStage == 8, "instructions per stage");
 
 struct FusedArgs {
   const uint16_t* x;          // [T, H*D] BF16
