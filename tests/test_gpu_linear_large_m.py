@@ -19,11 +19,11 @@ pytestmark = [pytest.mark.gpu, requires_gpu, pytest.mark.timeout(600)]
 N = 5120
 
 
-def _case(M, K):
-    rng = np.random.default_rng(7000 + M + K)
+def _case(M, K, n=N):
+    rng = np.random.default_rng(7000 + M + K + n)
     x = workloads.activations(rng, M, K)
-    w = workloads.weight_codes(rng, (N, K))
-    ws = workloads.scale_bytes(rng, (N, K // 32), -10, -4)
+    w = workloads.weight_codes(rng, (n, K))
+    ws = workloads.scale_bytes(rng, (n, K // 32), -10, -4)
     return x, w, ws
 
 
@@ -70,3 +70,16 @@ def test_block32_tiles_match_ring_kernel_at_64_rows():
     ref = G.mx_linear(x, w, ws, 32)
     assert_gemm_close(host_u16(a), ref[:64], "64 rows, decode kernels")
     assert_gemm_close(host_u16(b), ref, "65 rows, tiled kernel")
+
+
+@pytest.mark.parametrize("M,n,K", [(200, 1040, 288), (3000, 400, 96), (129, 16, 32), (8192, 272, 576)])
+def test_bf16_tiles_ragged_m_and_n(M, n, K):
+    """The BF16 branch's tiled kernel where neither M nor N fills its tiles
+    (both tile widths: 128 x 128 and 128 x 256), down to one 32-element K
+    step and a single 16-column weight."""
+    x, w, ws = _case(M, K, n)
+    wd = mx.mx_dequant_mxfp8_to_bf16(dev_u8(w), dev_u8(ws))
+    say("linear BF16 tiles, ragged", M, n, K)
+    out = mx.mx_linear(dev_u16(x), wd)
+    torch.cuda.synchronize()
+    assert_gemm_close(host_u16(out), G.mx_linear(x, w, ws, 32), f"M={M} N={n} K={K}")
