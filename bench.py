@@ -14,9 +14,10 @@ Printed: one JSON line -- the headline, with `roofline` for the GEMM
 oracle's), then `secondary`: the decode batch, the MXFP8 linear at its four
 K (64 rows, and 8192 rows at N = 5120) and the 100,000-token chunked
 prefill (OCP and FNUZ), each with its
-roofline fraction, the oracle's time and a parity record.  --extra adds the
-production down_proj, the load-time dequant and the BF16 arm.  Progress goes
-to stderr.  The exit status is 3 if any parity record fails.
+roofline fraction, the oracle's time and a parity record, then the
+production down_proj, the load-time dequant and the BF16 arm (the path the
+FP8 one replaces).  The decode GEMM and the decode-M linear are also set
+against a read-only stream of the same weights.  Progress goes to stderr.  The exit status is 3 if any parity record fails.
 
 Timing: whole steps run back to back for --settle-ms of wall time (the
 clocks and power settle under this load), then W untimed warm-up steps, then
@@ -24,7 +25,7 @@ K timed steps; no timed step is dropped.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
                        [--no-cpu-baseline] [--cpu-tokens N] [--no-secondary]
-                       [--extra] [--copy-calibration]
+                       [--copy-calibration]
 """
 
 import argparse
@@ -324,6 +325,19 @@ def bench_decode(mx, torch, workloads, cpu, calls=40):
             mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, q=q, scale=s)
             mx.mx_bmm_a8w8_mxscale(qv, sv, w, sw, out=out)
     us_graph = time_graph(torch, rec, calls)
+    # the GEMM alone in the same graph shape, and the read-only stream floor
+    # of its cold weights (one pass over each copy, nothing computed)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def rec_bmm():
+        for w, sw in wts:
+            mx.mx_bmm_a8w8_mxscale(qv, sv, w, sw, out=out)
+
+    def rec_floor():
+        for w, _ in wts:
+            mx.mx_stream_read(w, sink)
+    us_bmm_graph = time_graph(torch, rec_bmm, calls)
+    us_floor = time_graph(torch, rec_floor, calls)
     mx.mx_inv_rope_group_quant(x, pos, cosd, sind, p.H, p.D, 64, q=q, scale=s)
     mx.mx_bmm_a8w8_mxscale(qv, sv, w0, ws0, out=out)
     torch.cuda.synchronize()
@@ -340,7 +354,12 @@ def bench_decode(mx, torch, workloads, cpu, calls=40):
                  "TFLOPs": p.flops / us_b / 1e6, "weights": f"cold ({calls} rotating copies)"},
          "graph_40_calls": {"us_per_call": us_graph, "GBps": (bb + qb) / us_graph / 1e3,
                             "hbm_frac": (bb + qb) / us_graph / 1e3 / PEAK_HBM_GBS,
-                            "note": "quantiser + GEMM per call, one weight per call"}}
+                            "note": "quantiser + GEMM per call, one weight per call"},
+         "bmm_graph_40_calls": {"us_per_call": us_bmm_graph, "GBps": bb / us_bmm_graph / 1e3,
+                                "vs_stream_floor": us_bmm_graph / us_floor},
+         "stream_floor": {"us_per_call": us_floor, "GBps": p.G * p.N * p.K / us_floor / 1e3,
+                          "bytes": p.G * p.N * p.K,
+                          "note": "mx_stream_read over the same 40 cold weight copies, 40-call graph"}}
     if cpu:
         from oracle.gemm import bmm_a8w8_mxscale
         from oracle.quant import inv_rope_group_quant
@@ -397,10 +416,19 @@ def bench_linear(mx, torch, workloads, cpu, calls=40):
             for w, sw in wl:
                 mx.mx_linear(xd, w, sw, out=o, workspace=wsp)
         us = time_graph(torch, rec_lin, calls)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def rec_floor():
+            for w, _ in wl:
+                mx.mx_stream_read(w, sink)
+        us_floor = time_graph(torch, rec_floor, calls)
         lb = wbytes + M * K * 2 + M * N * 2
         rec["linear"] = {"us_per_call": us, "GBps": lb / us / 1e3,
                          "roofline": {"bound": "hbm", "frac": lb / us / 1e3 / PEAK_HBM_GBS, "algorithmic_bytes": lb},
+                         "vs_stream_floor": us / us_floor,
                          "note": "40-call graph, one weight per call"}
+        rec["stream_floor"] = {"us_per_call": us_floor, "bytes": wl[0][0].numel() * eb,
+                               "note": "mx_stream_read over the same weights, 40-call graph"}
         mx.mx_linear(xd, wl[0][0], wl[0][1], out=o, workspace=wsp)
         torch.cuda.synchronize()
         gout = o.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -543,8 +571,8 @@ def bench_long(mx, torch, workloads, cpu):
 
 
 def bench_extra(mx, torch, workloads, fp8_step_us, fp8_bmm_us, decode_bmm_us):
-    """--extra: the BF16 arm, the pages' production down_proj in 40-call
-    graphs and the load-time dequantisation of its 5120 x 576 weight."""
+    """The BF16 arm, the pages' production down_proj in 40-call graphs and
+    the load-time dequantisation of its 5120 x 576 weight."""
     res = {"graph_40_calls": bench_graphs(mx, torch, workloads),
            "bf16_arm": bench_bf16_arm(mx, torch, workloads, fp8_step_us, fp8_bmm_us, decode_bmm_us)}
     return res
@@ -680,9 +708,8 @@ def main():
                     help="skip every oracle leg (the CPU baseline and all parity records)")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-secondary", action="store_true",
-                    help="skip the decode batch, MXFP8 linear and 100,000-token stream records")
-    ap.add_argument("--extra", action="store_true",
-                    help="also time the production down_proj, the load-time dequant and the BF16 arm")
+                    help="skip the records beside the prefill chunk: decode batch, MXFP8 linear, 100,000-token "
+                         "stream, production down_proj, load-time dequant and the BF16 arm")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with three plain 1 GiB device-to-device copies (the reference kernel for "
                          "scaling HBM byte counters)")
@@ -797,7 +824,7 @@ def main():
         parity_ok &= all(x["pass"] for x in parities if x is not None)
         parity_ok &= all(lng["fnuz_vs_ocp_last_chunk"].values())
         torch.cuda.empty_cache()
-    if args.extra:
+    if not args.no_secondary:
         log("[bench] production down_proj, load-time dequant, BF16 arm")
         dec_us = rec.get("secondary", {}).get("decode_T64", {}).get("bmm", {}).get("us", float("nan"))
         rec["extra"] = bench_extra(mx, torch, workloads, ms_step * 1e3, b_avg_ms * 1e3, dec_us)

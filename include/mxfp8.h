@@ -339,9 +339,28 @@ mx_status mx_f32_to_e4m3_fnuz(const float* in, uint8_t* out, int64_t n);
 mx_status mx_f32_to_e4m3_device(const float* in, uint8_t* out, int64_t n, int32_t fmt,
                                 void* stream);
 
-/* e4m3 / E8M0 bytes -> FP32 (host).  Exact; NaN codes give NaN. */
+/* e4m3 / E8M0 bytes -> FP32 (host).  Exact; NaN codes give NaN.  The byte
+ * meanings are those the encoders above produce: e4m3 in the OCP or FNUZ
+ * encoding picked by `fmt` ([FNUZ], Purpose: gfx950 stores OCP bytes, gfx942
+ * FNUZ bytes with largest finite 224, and its reference checks decode a byte
+ * under the encoding the kernel wrote it in), E8M0 a biased power-of-two
+ * exponent, 2^(byte - 127), 0xFF NaN ([WOA], Implementation: the scales are
+ * biased E8M0 exponent bytes). */
 mx_status mx_e4m3_to_f32(const uint8_t* in, float* out, int64_t n, int32_t fmt);
 mx_status mx_e8m0_to_f32(const uint8_t* in, float* out, int64_t n);
+
+/* ------------------------------------------------------------- measurement */
+
+/*
+ * Reads `bytes` (a multiple of 16) at device address `src` once and discards
+ * them: the HBM floor that the weight-streaming calls (the decode-batch GEMM,
+ * the MXFP8 linear at decode M) are timed against on the same buffers.  No
+ * step of the FP8 path.  `sink` is a device uint32 that is written only when
+ * the XOR of a lane's words hits one fixed value (so that the loads cannot be
+ * dropped); its content means nothing.  src 16-byte aligned, sink 4-byte
+ * aligned.  Asynchronous on `stream`.
+ */
+mx_status mx_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ __all__ = [
     "mx_inv_rope_bf16", "mx_bmm_bf16", "mx_woa_expand_scales", "MX_SCALE_E8M0", "MX_SCALE_F32",
     "mx_f32_pow2_to_e8m0", "mx_f32_pow2_to_e8m0_device", "mx_f32_to_e4m3_ocp",
     "mx_f32_to_e4m3_fnuz", "mx_f32_to_e4m3_device", "mx_e4m3_to_f32", "mx_e8m0_to_f32",
-    "COUNTER_NAMES",
+    "mx_stream_read", "COUNTER_NAMES",
 ]
 
 MX_OK, MX_ERR_INVALID_ARG, MX_ERR_UNSUPPORTED, MX_ERR_NOT_LOSSLESS, MX_ERR_HIP = range(5)
@@ -83,6 +83,7 @@ def lib():
             "mx_linear_workspace_bytes": (SZ, [I64, I64, I64, I32]),
             "mx_linear": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P, SZ, P]),
             "mx_linear_noalloc": (ctypes.c_int, [P, I64, I64, P, P, I32, I64, P, P]),
+            "mx_stream_read": (ctypes.c_int, [P, I64, P, P]),
             "mx_f32_pow2_to_e8m0": (ctypes.c_int, [P, P, I64]),
             "mx_f32_pow2_to_e8m0_device": (ctypes.c_int, [P, P, I64, P, P]),
             "mx_f32_to_e4m3_ocp": (ctypes.c_int, [P, P, I64]),
@@ -319,6 +320,21 @@ def mx_bmm_bf16(x, w, out=None):
         out = torch.empty((T, G, N), dtype=torch.bfloat16, device=x.device)
     _check(lib().mx_bmm_bf16(_dev(x, "x", 2), _dev(w, "w", 2), _dev(out, "out", 2), T, G, N, K, _stream(x)))
     return out
+
+
+# ------------------------------------------------------- measurement
+
+def mx_stream_read(src, sink):
+    """One read-only pass over the device tensor `src` (its bytes a multiple
+    of 16): the HBM floor for weight-streaming calls.  `sink` is a device
+    int32/uint32 tensor of at least one element, written only by chance."""
+    nbytes = src.numel() * src.element_size()
+    if nbytes % 16:
+        raise ValueError(f"src has {nbytes} bytes, not a multiple of 16")
+    if not isinstance(sink, torch.Tensor) or sink.numel() < 1:
+        raise ValueError("sink must be a tensor of at least one element")
+    _same_device(src, ("sink", sink))
+    _check(lib().mx_stream_read(_dev(src, "src", src.element_size()), nbytes, _dev(sink, "sink", 4), _stream(src)))
 
 
 # ------------------------------------------------------- MXFP8 linear

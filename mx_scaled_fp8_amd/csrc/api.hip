@@ -37,6 +37,7 @@ mx_status launch_bmm_bf16(const void* x, const void* w, void* out, int64_t T, in
                           hipStream_t stream);
 mx_status launch_expand_scales(const void* in, int32_t kind, int32_t block_n, int32_t G, int32_t N, int32_t K,
                                uint8_t* out, int32_t* reject_count, hipStream_t stream);
+mx_status launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* cos, const void* sin,
                            int64_t max_pos, int64_t T, int32_t H, int32_t D, int32_t rope_dim, int32_t style,
                            const uint8_t* w, const uint8_t* w_scale, void* out, int32_t G, int32_t N,
@@ -334,6 +335,19 @@ mx_status mx_dequant_mxfp8_to_bf16(const uint8_t* w, const uint8_t* w_scale, voi
   MX_PREAMBLE();
   count(C_DEQUANT);
   const mx_status st = launch_dequant(w, w_scale, out, N, K, block, static_cast<hipStream_t>(stream));
+  if (st == MX_OK) clear_error();
+  return st;
+}
+
+mx_status mx_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  const char* fn = "mx_stream_read";
+  MX_CHECK(bytes >= 0 && bytes % 16 == 0, "%s: bytes = %lld is not a non-negative multiple of 16", fn,
+           (long long)bytes);
+  if (bytes == 0) { clear_error(); return MX_OK; }
+  MX_CHECK(src && sink, "%s: null pointer", fn);
+  MX_CHECK(aligned(src, 16) && aligned(sink, 4), "%s: src must be 16-byte and sink 4-byte aligned", fn);
+  MX_PREAMBLE();
+  const mx_status st = launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream));
   if (st == MX_OK) clear_error();
   return st;
 }

@@ -45,6 +45,7 @@ mx_status launch_expand_scales(const void*, int32_t, int32_t, int32_t, int32_t, 
 mx_status launch_woa_fused(const void*, const int64_t*, const void*, const void*, int64_t, int64_t, int32_t, int32_t,
                            int32_t, int32_t, const uint8_t*, const uint8_t*, void*, int32_t, int32_t,
                            hipStream_t) STUB()
+mx_status launch_stream_read(const void*, int64_t, uint32_t*, hipStream_t) STUB()
 }  // namespace mx
 
 static int failures = 0;
@@ -115,6 +116,8 @@ int main() {
   EXPECT(mx_linear(P, 1, int64_t(1) << 31, P, dummy, 2, 16, P, nullptr, 0, nullptr) == MX_ERR_INVALID_ARG);
   EXPECT(mx_linear_noalloc(P, 64, 1152, P, dummy, 1, 4096, P, nullptr) == MX_OK);
   EXPECT(mx_linear_noalloc(P, 1, 1056, P, dummy, 1, 16384, P, nullptr) == MX_ERR_INVALID_ARG);
+  EXPECT(mx_stream_read(P, 1 << 20, reinterpret_cast<uint32_t*>(dummy), nullptr) == MX_OK);
+  EXPECT(mx_stream_read(P, 24, reinterpret_cast<uint32_t*>(dummy), nullptr) == MX_ERR_INVALID_ARG);
   EXPECT(mx_woa_expand_scales(dummy, 0, 128, 2, 256, 512, dummy, nullptr, nullptr) == MX_OK);
   EXPECT(mx_woa_expand_scales(dummy, 1, 7, 2, 256, 512, dummy, nullptr, nullptr) == MX_ERR_INVALID_ARG);
   EXPECT(mx_f32_pow2_to_e8m0_device(reinterpret_cast<const float*>(dummy), dummy, 16, nullptr, nullptr) == MX_OK);

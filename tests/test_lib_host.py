@@ -272,3 +272,15 @@ def test_linear_noalloc_validation(dry):
     assert f(K=100) == mx.MX_ERR_INVALID_ARG
     assert f(s=None) == mx.MX_ERR_INVALID_ARG
     assert f(M=0, x=None) == mx.MX_OK
+
+
+def test_stream_read_validation(dry):
+    def f(src=FAKE, nbytes=1 << 20, sink=FAKE):
+        return _call("mx_stream_read", src, nbytes, sink, None)
+    assert f() == mx.MX_OK
+    assert f(nbytes=0, src=None, sink=None) == mx.MX_OK
+    assert f(nbytes=24) == mx.MX_ERR_INVALID_ARG                     # not a multiple of 16
+    assert f(nbytes=-16) == mx.MX_ERR_INVALID_ARG
+    assert f(src=FAKE + 8) == mx.MX_ERR_INVALID_ARG                  # src not 16-byte aligned
+    assert f(sink=FAKE + 2) == mx.MX_ERR_INVALID_ARG                 # sink not 4-byte aligned
+    assert f(sink=None) == mx.MX_ERR_INVALID_ARG
