@@ -140,7 +140,12 @@ mx_status mx_inv_rope_group_quant(const void* x, const int64_t* positions,
  * a        device u8 [T, G, K]: e4m3 codes in flavour a_fmt.
  * a_scale  device u8 [T, G, K/128].
  * a_fmt    MX_FP8_E4M3_OCP or MX_FP8_E4M3_FNUZ (an FNUZ code c times 2^s equals the OCP
- *          code c times 2^(s-1); FNUZ 0x80 (NaN) is not expected in A).
+ *          code c times 2^(s-1), so FNUZ blocks run on the OCP MFMA with their
+ *          scale byte lowered by one; FNUZ 0x80 (NaN) is not expected in A).
+ *          Exception: an FNUZ block with scale byte 0 (2^-127) would need the
+ *          OCP scale 2^-128, which E8M0 lacks; the byte is kept, so such a
+ *          block enters the sum at twice its value.  The quantiser writes byte
+ *          0 only for FNUZ groups with 0 < amax <= 224 * 2^-127.
  * w        device u8 [G, N, K]: OCP e4m3 codes (the checkpoint format).
  * w_scale  device u8 [G, N, K/128].
  * out      device BF16 [T, G, N].

@@ -8,6 +8,8 @@ decode batch and the 8192-token prefill chunk at full size with sampled rows
 checked, and run-to-run determinism.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -191,6 +193,35 @@ def test_fnuz_activations(T):
     ref = G.bmm_a8w8_mxscale(a_fnuz, sa_fnuz, w, sw, a_fmt=F.FNUZ)
     assert_gemm_close(o_fnuz, ref, "fnuz")
     assert np.array_equal(o_ocp, o_fnuz)
+
+
+@pytest.mark.parametrize("T,Gn,N,K", [(8, 2, 64, 1024), (40, 2, 64, 384), (300, 1, 256, 512), (512, 2, 256, 2048)])
+def test_fnuz_scale_byte_zero_is_computed_at_twice_its_value(T, Gn, N, K):
+    """The one FNUZ block the OCP MFMA cannot express: scale byte 0 (2^-127)
+    would need the OCP scale 2^-128, which E8M0 does not have, so the kernels
+    keep the byte and such a block comes out twice its value (the header
+    states this).  Every third token has all its blocks at byte 0; those rows
+    equal twice the oracle's FNUZ result within the bound and lie outside the
+    bound of the oracle's own; the other rows match the oracle.  The decode,
+    small-T, large-tile and persistent kernels all take this path."""
+    rng = np.random.default_rng(900 + T + K)
+    a, sa, w, sw = workloads.gemm_operands(901 + T, T, Gn, N, K, a_exp=(-12, -2))
+    a = np.where(a == 0x80, 0, a).astype(np.uint8)          # no FNUZ NaN in A
+    sa = rng.integers(120, 126, size=sa.shape).astype(np.uint8)
+    zero_rows = np.arange(0, T, 3)
+    sa[zero_rows] = 0
+    sw = rng.integers(200, 206, size=sw.shape).astype(np.uint8)   # lifts the 2^-127 blocks into range
+    say("bmm fnuz scale byte 0", T, Gn, N, K)
+    out = _gpu_bmm(a, sa, w, sw, mx.MX_FP8_E4M3_FNUZ)
+    ref = G.bmm_a8w8_mxscale(a, sa, w, sw, a_fmt=F.FNUZ)
+    other = np.setdiff1d(np.arange(T), zero_rows)
+    assert_gemm_close(out[other], ref[other], "rows with normal scales")
+    assert_gemm_close(out[zero_rows], 2.0 * ref[zero_rows], "scale-0 rows against twice the oracle")
+    g = F.bf16_to_f64(out[zero_rows])
+    r = ref[zero_rows]
+    rms = math.sqrt(float(np.mean(r * r)))
+    outside = np.abs(g - r) > 2.0 ** -7 * np.abs(r) + 1e-3 * rms
+    assert outside.mean() > 0.9                           # not within the oracle's own bound
 
 
 def test_deterministic():
