@@ -32,8 +32,9 @@ typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;                       // chunks of 8 elements per lane
-constexpr int kChunksPerBlock = kThreads * kUnroll;
+// chunks of 8 elements per lane: 4 for large inputs; 1 when that would leave
+// the chip with few workgroups (a decode batch, a linear's x)
+constexpr int kUnrollLarge = 4, kUnrollSmall = 1;
 
 struct QuantArgs {
   const uint4* x;             // [T, L] BF16 as 16-byte chunks
@@ -180,19 +181,19 @@ __device__ __forceinline__ uint2 encode8_ldexp(const uint4 v, int sh) {
 // unroll step u.  With 512-wide heads a segment is one head, so all its
 // rotated chunks (the last 8) fall in step u = 3 and the rotation code runs
 // in one step of four.
-template <int GROUP, int FMT, int STYLE, bool ROPE>
+template <int GROUP, int FMT, int STYLE, bool ROPE, int U>
 __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   constexpr int kLanesPerGroup = GROUP / 8;
   constexpr int EM = FMT == MX_FP8_E4M3_OCP ? 8 : 7;
   const uint32_t seg = blockIdx.x * (kThreads / 16) + (threadIdx.x >> 4);
-  const uint32_t base = seg * 64 + (threadIdx.x & 15);
-  uint4 v[kUnroll];
-  uint32_t cidx[kUnroll];
+  const uint32_t base = seg * (16 * U) + (threadIdx.x & 15);
+  uint4 v[U];
+  uint32_t cidx[U];
   // issue all loads first; out-of-range chunks re-read the last valid chunk so
   // that every lane takes part in the group reductions (a group is either all
   // in range or all out)
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const uint32_t c = base + u * 16;
     cidx[u] = c < a.total_chunks ? c : a.total_chunks - 1;
     // the input is read once and the codes written once: non-temporal
@@ -209,9 +210,9 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     p = a.pos[row];
     ok = p >= 0 && p < a.max_pos;
   }
-  uint32_t sword = 0;                   // group 128: the scale bytes of this row's 4 groups
+  uint32_t sword = 0;                   // group 128: the scale bytes of this row's U groups
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const uint32_t c = cidx[u];
     if constexpr (ROPE) {
       uint32_t cin = cin0 + u * 16;
@@ -262,15 +263,15 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
     }
   }
   if constexpr (GROUP == 128) {
-    // a row of 16 lanes quantised the 4 consecutive groups of its segment:
-    // their scale bytes leave as one 4-byte store
+    // a row of 16 lanes quantised the U consecutive groups of its segment:
+    // with U = 4 their scale bytes leave as one 4-byte store
     if ((threadIdx.x & 15) == 0) {
       uint8_t* dst = a.scale + base / 16;
-      if (base + 48 < a.total_chunks && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+      if (U == 4 && base + 48 < a.total_chunks && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
         *reinterpret_cast<uint32_t*>(dst) = sword;
       } else {
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int u = 0; u < U; ++u)
           if (base + u * 16 < a.total_chunks) dst[u] = static_cast<uint8_t>(sword >> (8 * u));
       }
     }
@@ -384,14 +385,27 @@ __global__ __launch_bounds__(kThreads) void rope_bf16_kernel(RopeArgs a) {
   }
 }
 
-template <int GROUP, int FMT>
-void launch_style(const QuantArgs& a, bool rope, int style, uint32_t blocks, hipStream_t s) {
+template <int GROUP, int FMT, int U>
+void launch_style_u(const QuantArgs& a, bool rope, int style, hipStream_t s) {
+  const uint32_t blocks = static_cast<uint32_t>((a.total_chunks + kThreads * U - 1) / (kThreads * U));
   if (!rope)
-    quant_kernel<GROUP, FMT, MX_ROPE_INTERLEAVED, false><<<blocks, kThreads, 0, s>>>(a);
+    quant_kernel<GROUP, FMT, MX_ROPE_INTERLEAVED, false, U><<<blocks, kThreads, 0, s>>>(a);
   else if (style == MX_ROPE_INTERLEAVED)
-    quant_kernel<GROUP, FMT, MX_ROPE_INTERLEAVED, true><<<blocks, kThreads, 0, s>>>(a);
+    quant_kernel<GROUP, FMT, MX_ROPE_INTERLEAVED, true, U><<<blocks, kThreads, 0, s>>>(a);
   else
-    quant_kernel<GROUP, FMT, MX_ROPE_NEOX, true><<<blocks, kThreads, 0, s>>>(a);
+    quant_kernel<GROUP, FMT, MX_ROPE_NEOX, true, U><<<blocks, kThreads, 0, s>>>(a);
+}
+
+#ifndef QUANT_SMALL_BLOCKS
+#define QUANT_SMALL_BLOCKS 1024
+#endif
+template <int GROUP, int FMT>
+void launch_style(const QuantArgs& a, bool rope, int style, hipStream_t s) {
+  // fewer than this many workgroups at 4 chunks per lane: 1 chunk per lane
+  if ((a.total_chunks + kThreads * kUnrollLarge - 1) / (kThreads * kUnrollLarge) < QUANT_SMALL_BLOCKS)
+    launch_style_u<GROUP, FMT, kUnrollSmall>(a, rope, style, s);
+  else
+    launch_style_u<GROUP, FMT, kUnrollLarge>(a, rope, style, s);
 }
 
 int log2_if_pow2(uint32_t v) {
@@ -429,14 +443,13 @@ mx_status launch_quant(const void* x, const int64_t* positions, const void* cos,
     a.half_pairs = static_cast<uint32_t>(rope_dim / 2);
     a.q = reinterpret_cast<uint2*>(q + r0 * L);
     a.scale = scale + r0 * (L / group);
-    const uint32_t blocks = static_cast<uint32_t>((a.total_chunks + kChunksPerBlock - 1) / kChunksPerBlock);
     const bool rope = rope_dim > 0;
     if (group == 128) {
-      if (fmt == MX_FP8_E4M3_OCP) launch_style<128, MX_FP8_E4M3_OCP>(a, rope, style, blocks, stream);
-      else launch_style<128, MX_FP8_E4M3_FNUZ>(a, rope, style, blocks, stream);
+      if (fmt == MX_FP8_E4M3_OCP) launch_style<128, MX_FP8_E4M3_OCP>(a, rope, style, stream);
+      else launch_style<128, MX_FP8_E4M3_FNUZ>(a, rope, style, stream);
     } else {
-      if (fmt == MX_FP8_E4M3_OCP) launch_style<32, MX_FP8_E4M3_OCP>(a, rope, style, blocks, stream);
-      else launch_style<32, MX_FP8_E4M3_FNUZ>(a, rope, style, blocks, stream);
+      if (fmt == MX_FP8_E4M3_OCP) launch_style<32, MX_FP8_E4M3_OCP>(a, rope, style, stream);
+      else launch_style<32, MX_FP8_E4M3_FNUZ>(a, rope, style, stream);
     }
     const mx_status st = launch_status("mx_inv_rope_group_quant");
     if (st != MX_OK) return st;
