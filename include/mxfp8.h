@@ -287,8 +287,10 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t w_elem
  * workspace device, at least mx_linear_workspace_bytes(M, N, K, w_elem_bytes),
  *          16-byte aligned (may be NULL when that is 0).
  * Requires: M, N >= 0, K > 0, K % 32 == 0, N % 16 == 0, x/w 16-byte aligned,
- * out 8-byte aligned.  Any M: up to 64 rows (a decode batch) run on kernels that
- * keep the weight streaming, more rows (a prefill chunk) on 256 x 256 tiles.
+ * out 8-byte aligned; M <= 2^30, N and K < 2^31, M*K, N*K and M*N < 2^40.
+ * Any M: up to 64 rows (a decode batch) run on kernels that keep the weight
+ * streaming, more rows (a prefill chunk) on tiles with operand reuse (256 x 256
+ * block-scaled FP8 tiles; 128 x 256 or 128 x 128 BF16 tiles).
  */
 mx_status mx_linear(const void* x, int64_t M, int64_t K, const void* w,
                     const uint8_t* w_scale, int32_t w_elem_bytes, int64_t N, void* out,

@@ -376,9 +376,10 @@ mx_status linear_check(const char* fn, const void* x, int64_t M, int64_t K, cons
   MX_CHECK(K % MX_LINEAR_BLOCK == 0, "%s: K = %lld is not a multiple of %d", fn, (long long)K, MX_LINEAR_BLOCK);
   MX_CHECK(N % 16 == 0, "%s: N = %lld is not a multiple of 16", fn, (long long)N);
   MX_CHECK(w_elem_bytes == 1 || w_elem_bytes == 2, "%s: w_elem_bytes = %d (1 = FP8, 2 = BF16)", fn, w_elem_bytes);
-  // the kernels index K, M*K and N*K with 32-bit and 40-bit offsets
-  MX_CHECK(M <= (int64_t(1) << 30) && K < (int64_t(1) << 31) && N * K < (int64_t(1) << 40) &&
-               M * K < (int64_t(1) << 40),
+  // the kernels index K, M*K, N*K and M*N with 32-bit and 40-bit offsets,
+  // and take N as a 32-bit value
+  MX_CHECK(M <= (int64_t(1) << 30) && N < (int64_t(1) << 31) && K < (int64_t(1) << 31) &&
+               N * K < (int64_t(1) << 40) && M * K < (int64_t(1) << 40) && M * N < (int64_t(1) << 40),
            "%s: shape too large (M = %lld, N = %lld, K = %lld)", fn, (long long)M, (long long)N, (long long)K);
   if (M == 0 || N == 0) return MX_OK;
   MX_CHECK(x && w && out, "%s: null tensor pointer", fn);

@@ -185,10 +185,12 @@ __device__ __forceinline__ void tiled_issue(uint8_t* sl, int w_bytes, const uint
                                             const uint8_t* const (&gx)[XD], int kt, int wave) {
 #pragma unroll
   for (int u = 0; u < WD; ++u)
-    __builtin_amdgcn_global_load_lds(gw[u] + kt * kTRow, (lds_void_t*)(sl + (WD * wave + u) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gw[u] + static_cast<size_t>(kt) * kTRow, (lds_void_t*)(sl + (WD * wave + u) * 1024),
+                                     16, 0, 0);
 #pragma unroll
   for (int u = 0; u < XD; ++u)
-    __builtin_amdgcn_global_load_lds(gx[u] + kt * kTRow, (lds_void_t*)(sl + w_bytes + (XD * wave + u) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(gx[u] + static_cast<size_t>(kt) * kTRow,
+                                     (lds_void_t*)(sl + w_bytes + (XD * wave + u) * 1024), 16, 0, 0);
 }
 
 template <int NI, int SLOTS>

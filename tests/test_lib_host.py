@@ -192,6 +192,8 @@ def test_linear_validation(dry):
     # K on its own past 2^31 (N small enough for N*K): rejected before any
     # kernel narrows it to 32 bits
     assert f(K=1 << 31, N=16, M=1, eb=2, ws=None, wsb=0) == mx.MX_ERR_INVALID_ARG
+    assert f(K=32, N=1 << 31, M=1, eb=2, ws=None, wsb=0) == mx.MX_ERR_INVALID_ARG     # N past 32 bits
+    assert f(K=32, N=1 << 20, M=1 << 20, eb=2, ws=None, wsb=0) == mx.MX_ERR_INVALID_ARG   # M*N = 2^40
 
 
 def _rope_bf16(**kw):
