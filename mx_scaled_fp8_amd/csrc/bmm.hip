@@ -38,7 +38,7 @@
 //    tile boundaries and stores each tile through LDS as 128-byte row pieces
 //    while the next tile's first MFMAs run.
 //  * bmm_decode_kernel (T <= 64, K of 1024 to 8192): one workgroup per
-//    (g, 64 n) with all T rows; both operands through an LDS-DMA ring of 8
+//    (g, 64 n) with all T rows; both operands through an LDS-DMA ring of 4
 //    K-steps; the waves split n.  A BF16 mode serves the BF16 arm.
 //  * bmm_small_kernel (T <= 64, other K): the 4 waves split K, operands
 //    double-buffered in registers, partial sums reduced through LDS.
@@ -1161,14 +1161,16 @@ __global__ __launch_bounds__(kSmallThreads) void bmm_small_kernel(SmallArgs p) {
 // One workgroup per (g, 64 n) with all T rows, as bmm_small_kernel, but the
 // operands go global -> LDS by LDS-DMA through a ring of kDecR stages (one
 // 128-byte K-step of the 64 W rows and the 64 A rows each, 16 KiB), so that
-// kDecR - 1 K-steps (112 KiB) per compute unit are in flight and every DMA
-// instruction reads 8 whole 128-byte lines.  The four waves split n (wave w
+// kDecR - 1 K-steps (48 KiB) per compute unit are in flight and every DMA
+// instruction reads 8 whole 128-byte lines.  (8 stages, 112 KiB in flight,
+// were no faster: 17.4 against 17.2 us per call; the weight's access pattern,
+// all 64 rows advancing 128 bytes at a time, sets the pace.)  The four waves split n (wave w
 // owns rows 16w..16w+15 of the workgroup's W), so every wave consumes every
 // stage and no partial sums are reduced; one barrier per stage recycles the
 // ring.  Each slot is its own __shared__ array and the stage loop is unrolled
 // over the ring, so every access names its slot statically (the compiler can
 // then see that the DMA into one slot does not alias the reads of another).
-constexpr int kDecR = 8;
+constexpr int kDecR = 4;
 constexpr int kDecRows = 64;
 // operand modes of the decode kernel: FP8 A in OCP or FNUZ bytes (E8M0
 // scales), or BF16 A and W (no scales; a stage is then 64 elements and the
@@ -1191,15 +1193,19 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s1[kDecStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s2[kDecStage];
   __shared__ __attribute__((aligned(1024))) uint8_t s3[kDecStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s4[kDecStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s5[kDecStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s6[kDecStage];
-  __shared__ __attribute__((aligned(1024))) uint8_t s7[kDecStage];
   __shared__ __attribute__((aligned(16))) uint8_t scl[kDecScaleMax];   // [64 W rows | 64 A rows][KB]
-  uint8_t* const ring[kDecR] = {s0, s1, s2, s3, s4, s5, s6, s7};
+  uint8_t* const ring[kDecR] = {s0, s1, s2, s3};
+  static_assert(kDecR == 4, "one __shared__ array per ring slot");
 
-  const int g = blockIdx.x / p.n_groups;
-  const int n0 = (blockIdx.x % p.n_groups) * kDecRows;
+  // XCD-aware: workgroup b runs on XCD b % 8; when the work divides evenly,
+  // each XCD takes a contiguous range of (g, n-block) work items, so the
+  // workgroups sharing one group's activation rows share one XCD's L2
+  // (decode batch: 18.1 -> 17.4 us per call in a 40-call graph)
+  const int total = p.G * p.n_groups;
+  const int work = total % 8 == 0 ? static_cast<int>(blockIdx.x % 8) * (total / 8) + static_cast<int>(blockIdx.x / 8)
+                                  : static_cast<int>(blockIdx.x);
+  const int g = work / p.n_groups;
+  const int n0 = (work % p.n_groups) * kDecRows;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1262,7 +1268,7 @@ __global__ __launch_bounds__(256, 1) void bmm_decode_kernel(SmallArgs p) {
   // in flight (the scale DMA is older than all of them)
   constexpr int kDecDmaPerStage = 2 * 2;
   constexpr int kWaitStage = wait_vm(kDecDmaPerStage * (kDecR - 2));
-  static_assert(kWaitStage == 0x4078, "vmcnt(24)");
+  static_assert(kWaitStage == 0x0078, "vmcnt(8)");
 
 #pragma unroll 1
   for (int kt0 = 0; kt0 < KB; kt0 += kDecR) {
