@@ -32,9 +32,10 @@ typedef unsigned v4u_t __attribute__((ext_vector_type(4)));
 typedef unsigned v2u_t __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;
-// chunks of 8 elements per lane: 4 for large inputs; 1 when that would leave
-// the chip with few workgroups (a decode batch, a linear's x)
-constexpr int kUnrollLarge = 4, kUnrollSmall = 1;
+// chunks of 8 elements per lane: 2 for large inputs (8192-token chunk: 252
+// against 260 us with 4 and 274 with 8 per lane; 1 took 334); 1 when 2 would
+// leave the chip with few workgroups (a decode batch, a linear's x)
+constexpr int kUnrollLarge = 2, kUnrollSmall = 1;
 
 struct QuantArgs {
   const uint4* x;             // [T, L] BF16 as 16-byte chunks
@@ -264,11 +265,11 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(QuantArgs a) {
   }
   if constexpr (GROUP == 128) {
     // a row of 16 lanes quantised the U consecutive groups of its segment:
-    // with U = 4 their scale bytes leave as one 4-byte store
+    // with U = 2 their scale bytes leave as one 2-byte store
     if ((threadIdx.x & 15) == 0) {
       uint8_t* dst = a.scale + base / 16;
-      if (U == 4 && base + 48 < a.total_chunks && (reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
-        *reinterpret_cast<uint32_t*>(dst) = sword;
+      if (U == 2 && base + 16 < a.total_chunks && (reinterpret_cast<uintptr_t>(dst) & 1) == 0) {
+        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(sword);
       } else {
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -396,13 +397,11 @@ void launch_style_u(const QuantArgs& a, bool rope, int style, hipStream_t s) {
     quant_kernel<GROUP, FMT, MX_ROPE_NEOX, true, U><<<blocks, kThreads, 0, s>>>(a);
 }
 
-#ifndef QUANT_SMALL_BLOCKS
-#define QUANT_SMALL_BLOCKS 1024
-#endif
+constexpr uint32_t kSmallBlocks = 1024;
 template <int GROUP, int FMT>
 void launch_style(const QuantArgs& a, bool rope, int style, hipStream_t s) {
-  // fewer than this many workgroups at 4 chunks per lane: 1 chunk per lane
-  if ((a.total_chunks + kThreads * kUnrollLarge - 1) / (kThreads * kUnrollLarge) < QUANT_SMALL_BLOCKS)
+  // fewer than kSmallBlocks workgroups at kUnrollLarge chunks per lane: 1 chunk per lane
+  if ((a.total_chunks + kThreads * kUnrollLarge - 1) / (kThreads * kUnrollLarge) < kSmallBlocks)
     launch_style_u<GROUP, FMT, kUnrollSmall>(a, rope, style, s);
   else
     launch_style_u<GROUP, FMT, kUnrollLarge>(a, rope, style, s);
