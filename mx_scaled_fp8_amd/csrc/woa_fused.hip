@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int KB = p.K / kBK;                        // <= kMaxKB
   const int kb0 = (tt + nt) % KB;                  // K rotation, as bmm_large_kernel
   const int L = p.G * p.K;                         // elements per token row (H * D)
-  auto real_stage = [&](int kb) {
+  auto real_stage = [&](int kb) __attribute__((always_inline)) {
     int kr = kb + kb0;
     return kr >= KB ? kr - KB : kr;
   };
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // lane offset of row group 0 and the cap past which rows re-read the last one
   const uint32_t offW0 = static_cast<uint32_t>(dma_row) * static_cast<uint32_t>(p.K) + dma_chunk;
   const uint32_t capW = static_cast<uint32_t>(limW) * static_cast<uint32_t>(p.K) + dma_chunk;
-  auto issue_w = [&](uint8_t* buf, int kb) {
+  auto issue_w = [&](uint8_t* buf, int kb) __attribute__((always_inline)) {
     const uint8_t* bW = baseW + static_cast<uint32_t>(real_stage(kb)) * kBK;
 #pragma unroll
     for (int it = 0; it < kWDmaPerStage; ++it) {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int limT = p.T - 1 - t0;
   const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
   uint4 av[8][2];
-  auto load_a = [&](int kb) {
+  auto load_a = [&](int kb) __attribute__((always_inline)) {
     const uint8_t* base = xtile + real_stage(kb) * (2 * kBK);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int R = p.R;
   const int half = R >> 1;
   // is the stage at element offset `col` of group g the last 128 dims of a head?
-  auto rope_stage = [&](int kb) {
+  auto rope_stage = [&](int kb) __attribute__((always_inline)) {
     if constexpr (!ROPE) return false;
     const int colg = g * p.K + real_stage(kb) * kBK;
     return (colg + kBK) % p.D == 0;
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // row tr = arow0 + 8j is at + 1024 j, and its swizzle swz8(tr) depends on
   // tr % 16 only, so it is swz8(ri) for even j and swz8(ri) ^ 4 for odd j
   const int szr = swz8(ri);
-  auto piece_off = [&](int ch, int sz) { return (((ch >> 1) ^ sz) << 4) + (ch & 1) * 8; };
+  auto piece_off = [&](int ch, int sz) __attribute__((always_inline)) { return (((ch >> 1) ^ sz) << 4) + (ch & 1) * 8; };
   const uint32_t qoff[2][2] = {
       {static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr)),
        static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr ^ 4))},
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // rotation has read its tables, so no barrier is involved.  8 DMA
   // instructions per wave: 8 lanes (16-byte pieces) per row, 8 rows each;
   // pieces past the 2R bytes re-read the first (never used).
-  auto issue_cs = [&](uint8_t* buf, int kb) {
+  auto issue_cs = [&](uint8_t* buf, int kb) __attribute__((always_inline)) {
     if (!ROPE || !rope_stage(kb)) return;
     uint8_t* dst = buf + kOpBytes + wave * 64 * kBK;
     const int piece = lane & 7;
@@ -296,12 +296,12 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const bool rot_b = NEOX ? ca >= first_rot : cb >= first_rot;
   const int ti_a = NEOX ? (rot_a ? (ca - first_rot) * 8 : 0) : (rot_a ? (ca - first_rot) * 4 : 0);
   const int ti_b = NEOX ? ti_a : (rot_b ? (cb - first_rot) * 4 : 0);
-  auto rotate2 = [&](const uint8_t* tab, uint4& v0, uint4& v1) {
+  auto rotate2 = [&](const uint8_t* tab, uint4& v0, uint4& v1) __attribute__((always_inline)) {
     const uint16_t* crow = reinterpret_cast<const uint16_t*>(tab);
     const uint16_t* srow = crow + half;
     if constexpr (!NEOX) {
       // pairs (2i, 2i+1) of the rotated slice: a chunk's 4 dwords are 4 pairs
-      auto rot_chunk = [&](const uint4 v, const uint2 cc, const uint2 ss) {
+      auto rot_chunk = [&](const uint4 v, const uint2 cc, const uint2 ss) __attribute__((always_inline)) {
         float xr, yr;
         uint4 r;
         inv_rotate(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(cc.x), bf16_lo(ss.x), xr, yr);
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // quantise stage kb from av[]: `rot` rotates it first (a rope stage); the
   // two versions are separate code, chosen per stage, so that the rotation's
   // registers are needed only in the stages that rotate
-  auto quantise_v = [&](auto rot, uint8_t* buf, int sb) {
+  auto quantise_v = [&](auto rot, uint8_t* buf, int sb) __attribute__((always_inline)) {
     constexpr bool RS = decltype(rot)::value;
     const uint8_t* tab = buf + kOpBytes + arow0 * kBK;   // row group 0's tables (rope stage)
 #pragma unroll
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto quantise = [&](int kb, uint8_t* buf, int sb) {
+  auto quantise = [&](int kb, uint8_t* buf, int sb) __attribute__((always_inline)) {
     if (ROPE && rope_stage(kb))
       quantise_v(std::true_type{}, buf, sb);
     else
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int sz = swz8(r32);
   const int ch0[2] = {(q2 ^ sz) << 4, ((4 + q2) ^ sz) << 4};
   const int ch1[2] = {((q2 + 2) ^ sz) << 4, ((6 + q2) ^ sz) << 4};
-  auto read_frag = [&](const uint8_t* q, int h) {
+  auto read_frag = [&](const uint8_t* q, int h) __attribute__((always_inline)) {
     return make_v8i(*reinterpret_cast<const uint4*>(q + ch0[h]), *reinterpret_cast<const uint4*>(q + ch1[h]));
   };
 
@@ -402,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mma_stage = [&](const uint8_t* buf, int kb, int sb) {
+  auto mma_stage = [&](const uint8_t* buf, int kb, int sb) __attribute__((always_inline)) {
     const uint32_t swv = *reinterpret_cast<const uint32_t*>(&wsc[real_stage(kb)][wn][r32][0]);
     const uint32_t sav = *reinterpret_cast<const uint32_t*>(&asc[sb][wt][r32][0]);
 #pragma unroll
@@ -447,42 +447,41 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   issue_w(st0, 0);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
   stage_barrier();
+  quantise(0, st0, 0);
+  if (KB > 1) {                                      // stage 1 into the unused buffer
+    load_a(1);
+    issue_cs(st1, 1);
+    issue_w(st1, 1);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmMax);
+  stage_barrier();                                   // stage 0's codes are in st0
 
-  // ---- stage loop.  On entry to iteration kb >= 0: buffer kb%2 holds stage
-  // kb (W and the quantised A); this wave's loads of stage kb+1's BF16 and
-  // then the DMA of its W (into the other buffer) may be in flight.
-  // Iteration -1 only quantises stage 0 (its loads have landed) and starts
-  // stage 1.
-  for (int kb = -1; kb < KB; ++kb) {
+  // ---- stage loop.  On entry to iteration kb: buffer kb%2 holds stage kb
+  // (W and the quantised A); this wave's loads of stage kb+1's BF16, its
+  // rotation tables and then the DMA of its W (into the other buffer) may be
+  // in flight.  (The prologue above is outside the loop, and every lambda is
+  // inlined: with a first iteration that skipped the MFMAs, or with the
+  // quantiser as a called function, the register allocator moved the
+  // accumulators through scratch memory on every stage.)
+  for (int kb = 0; kb < KB; ++kb) {
     uint8_t* cur = (kb & 1) ? st1 : st0;
     uint8_t* nxt = (kb & 1) ? st0 : st1;
-    if (kb + 1 < KB) {
-      // stage kb+1's BF16 (and rotation tables) have landed once at most its
-      // W DMA is pending (at kb = -1 nothing is)
-      __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
-    }
-    if (kb >= 0) mma_stage(cur, kb, kb & 1);
-    if (kb + 1 < KB) {
+    const bool more = kb + 1 < KB;
+    // stage kb+1's BF16 and tables have landed once at most its W DMA is pending
+    if (more) __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
+    mma_stage(cur, kb, kb & 1);
+    if (more) {
       quantise(kb + 1, nxt, (kb + 1) & 1);
       if (kb + 2 < KB) {
         load_a(kb + 2);
-        if (kb < 0) {                             // stage 1: its buffer has not been used
-          issue_cs(cur, kb + 2);
-          issue_w(cur, kb + 2);
-        }
-        // stage kb+1's W has landed once at most stage kb+2's loads are
-        // pending (at kb = -1 stage 0's W landed before the loop, and
-        // stage 1's DMA above may stay in flight)
-        if (kb >= 0)
-          __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
-        else
-          __builtin_amdgcn_s_waitcnt(kWaitVmMax);
+        // stage kb+1's W has landed once at most stage kb+2's loads are pending
+        __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
       } else {
         __builtin_amdgcn_s_waitcnt(wait_vm(0));
       }
     }
     stage_barrier();                                 // everyone is done with `cur`; stage kb+1 is in `nxt`
-    if (kb >= 0 && kb + 2 < KB) {
+    if (kb + 2 < KB) {
       issue_cs(cur, kb + 2);
       issue_w(cur, kb + 2);
     }
