@@ -99,23 +99,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Writing amax = m * 2^E with m in [1, 2): e = E - EM + (m > 1.75), because
 // M * 2^(E-EM) = 1.75 * 2^E.  On BF16 bits m > 1.75 means mantissa field > 0x60.
 // Clamped to [-127, 127]; 0 gives -127.  amax must be finite (< 0x7F80).
+// Branch-free: a zero or subnormal amax (exponent field 0) has E <= -127, so
+// its e is below -127 whatever its mantissa and the clamp gives -127 -- the
+// same as the formula on the raw fields; and a finite amax (field <= 254)
+// gives at most 254 - 127 - 7 + 1 = 121, so the upper clamp never acts.
 template <int EM>
 __device__ __forceinline__ int e8m0_exponent(uint32_t amax_bits) {
-  const int ef = static_cast<int>(amax_bits >> 7);
-  const int mf = static_cast<int>(amax_bits & 0x7F);
-  int E, over;
-  if (ef != 0) {
-    E = ef - 127;
-    over = mf > 0x60;
-  } else {
-    // subnormal (or zero): value mf * 2^-133
-    const int bl = 32 - __clz(mf);              // bit length, 0 for zero
-    E = bl - 1 - 133;
-    over = ((mf << (8 - bl)) & 0x7F) > 0x60;
-  }
-  int e = E - EM + over;
-  if (amax_bits == 0) e = -127;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
+  const int e = static_cast<int>(amax_bits >> 7) - 127 - EM + ((amax_bits & 0x7F) > 0x60 ? 1 : 0);
+  return max(e, -127);
 }
 
 // Two floats -> two OCP e4m3 codes (round to nearest even) packed into the low

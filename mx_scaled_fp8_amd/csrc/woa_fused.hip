@@ -63,6 +63,28 @@ constexpr int kWDmaPerStage = kTile / 32;   // 8 row groups of 32 rows, one DMA 
 
 constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
 static_assert(kALoadsPerStage == 8 * 2 && kWDmaPerStage == 8, "instructions per stage");
+template <int N>
+using ic = std::integral_constant<int, N>;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;    // buffer resource word 3 (gfx9): 32-bit data format, no swizzle
+// calls f(ic<k>) for k = B .. E-1, in order
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+// Of the 32 MFMAs of a stage, the first kPure run before any quantisation
+// work and the rest go kPerGroup to a row group; MFMA q of a row group is
+// issued at point hook_of(kPerGroup, q) (0..3) of the group's work.
+#ifndef WOA_PURE_MFMAS
+#define WOA_PURE_MFMAS 16
+#endif
+constexpr int kPure = WOA_PURE_MFMAS;
+constexpr int kPerGroup = (32 - kPure) / 8;
+static_assert(kPure % 8 == 0 && kPerGroup >= 1 && kPerGroup <= 4, "MFMAs per row group");
+constexpr int hook_of(int per_group, int q) { return per_group == 2 ? 2 * q : q; }
 
 struct FusedArgs {
   const uint16_t* x;          // [T, H*D] BF16
@@ -134,7 +156,9 @@ __device__ __forceinline__ void inv_rotate(float x, float y, float c, float s, f
 
 // OCP codes of the 8 BF16 values of v divided by 2^e (sbits: E8M0 byte << 23)
 __device__ __forceinline__ uint2 encode8(const uint4 v, float sbits) {
-  v2s lo = {0, 0}, hi = {0, 0};
+  // both halves of lo and hi are written: their initial values are any bits
+  // at hand (v.x and v.y, so that the pair lands in adjacent registers)
+  v2s lo = __builtin_bit_cast(v2s, v.x), hi = __builtin_bit_cast(v2s, v.y);
   lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.x), sbits, false);
   lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lo, __builtin_bit_cast(v2bf, v.y), sbits, true);
   hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(hi, __builtin_bit_cast(v2bf, v.z), sbits, false);
@@ -151,6 +175,15 @@ __device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], co
                                                              static_cast<int>(swv), J, static_cast<int>(sav));
 }
 
+template <int IJ, int END>
+__device__ __forceinline__ void mfma_range(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+                                           uint32_t sav) {
+  if constexpr (IJ < END) {
+    mfma_ij<IJ / 4, IJ % 4>(acc, w, a, swv, sav);
+    mfma_range<IJ + 1, END>(acc, w, a, swv, sav);
+  }
+}
+
 template <int IJ = 0>
 __device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
                                          uint32_t sav) {
@@ -162,9 +195,14 @@ __device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&w)[4], c
 
 template <bool ROPE, bool NEOX>
 __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
-  // stage buffers: [W tile 256 x 128 B | A tile 256 x 128 B]
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[2 * kOpBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[2 * kOpBytes];
+  // stage buffers 0 and 1: W tile 256 x 128 B (sw) and A tile 256 x 128 B
+  // (sa), four separate arrays so that the compiler can tell the weight DMA
+  // from the activation codes and tables (with one array per stage it made
+  // the code stores and table reads wait for the weight DMA of the stage)
+  __shared__ __attribute__((aligned(1024))) uint8_t sw0[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sw1[kOpBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[kOpBytes];
   // W scales of every stage of the tile, [stage][wave half][row % 32][tile]
   __shared__ __attribute__((aligned(16))) uint8_t wsc[kMaxKB][2][32][4];
   // A scales of the stage in each buffer, [buffer][wave half][row % 32][tile]
@@ -200,14 +238,14 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // lane offset of row group 0 and the cap past which rows re-read the last one
   const uint32_t offW0 = static_cast<uint32_t>(dma_row) * static_cast<uint32_t>(p.K) + dma_chunk;
   const uint32_t capW = static_cast<uint32_t>(limW) * static_cast<uint32_t>(p.K) + dma_chunk;
-  auto issue_w = [&](uint8_t* buf, int kb) __attribute__((always_inline)) {
+  auto issue_w = [&](uint8_t* bw, int kb) __attribute__((always_inline)) {
     const uint8_t* bW = baseW + static_cast<uint32_t>(real_stage(kb)) * kBK;
 #pragma unroll
     for (int it = 0; it < kWDmaPerStage; ++it) {
       uint32_t b = offW0;
       asm volatile("" : "+v"(b));                    // formed per issue, not held as 8 addresses
       const uint32_t o = min(b + static_cast<uint32_t>(it * 32) * static_cast<uint32_t>(p.K), capW);
-      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(buf + (it * 32 + wave * 8) * kBK), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(bw + (it * 32 + wave * 8) * kBK), 16, 0, 0);
     }
   };
 
@@ -219,36 +257,53 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int ca = (c / cd) * 2 * cd + (c % cd);
   const int cb = ca + cd;
   const int arow0 = wave * 64 + ri;               // tile row of row group 0
-  // the tile's first row, group g: a wave-uniform base; lanes add a 32-bit
-  // offset (row * row bytes + chunk), rows past T clamped to the last one
-  const uint8_t* xtile = reinterpret_cast<const uint8_t*>(p.x + static_cast<size_t>(t0) * L +
-                                                          static_cast<size_t>(g) * p.K);
-  const int limT = p.T - 1 - t0;
+  // A goes through a buffer resource whose base is the tile's first row
+  // (group g's columns) and whose size ends at row T: rows past T read
+  // zeros (their outputs are never stored).  A lane's two offsets are fixed
+  // for the tile; the row group and the stage enter as the scalar offset, so
+  // a load costs no address arithmetic.  Offsets stay below 2^32: at most
+  // 255 rows of H*D < 2^23 BF16 plus one group's 2 K bytes.
   const uint32_t row_bytes = static_cast<uint32_t>(L) * 2;
+  const uint64_t valid_bytes = static_cast<uint64_t>(p.T - t0) * row_bytes;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.x + static_cast<size_t>(t0) * L + static_cast<size_t>(g) * p.K), 0,
+      static_cast<int>(min(valid_bytes, static_cast<uint64_t>(0xFFFFFFFFu))), kBufferFlags);
+  const uint32_t voff_a = static_cast<uint32_t>(arow0) * row_bytes + static_cast<uint32_t>(ca) * 16;
+  const uint32_t voff_b = voff_a + static_cast<uint32_t>(cd) * 16;
   uint4 av[8][2];
+  auto stage_soff = [&](int kb) __attribute__((always_inline)) {
+    return static_cast<uint32_t>(real_stage(kb)) * (2 * kBK);
+  };
+  // row group j (rows 64 wave + 8j + ri) of the stage at scalar offset soff into av[j]
+  auto load_group = [&](int j, uint32_t soff) __attribute__((always_inline)) {
+    const uint32_t so = soff + static_cast<uint32_t>(8 * j) * row_bytes;
+    const v4u a0 = __builtin_amdgcn_raw_buffer_load_b128(xres, static_cast<int>(voff_a), static_cast<int>(so), 0);
+    const v4u a1 = __builtin_amdgcn_raw_buffer_load_b128(xres, static_cast<int>(voff_b), static_cast<int>(so), 0);
+    av[j][0] = make_uint4(a0.x, a0.y, a0.z, a0.w);
+    av[j][1] = make_uint4(a1.x, a1.y, a1.z, a1.w);
+  };
   auto load_a = [&](int kb) __attribute__((always_inline)) {
-    const uint8_t* base = xtile + real_stage(kb) * (2 * kBK);
+    const uint32_t soff = stage_soff(kb);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint32_t r = static_cast<uint32_t>(min(arow0 + 8 * j, limT));
-      // formed here, not hoisted out of the loop as 8 live 64-bit addresses
-      asm volatile("" : "+v"(r));
-      const uint32_t o = r * row_bytes + static_cast<uint32_t>(ca) * 16;
-      av[j][0] = *reinterpret_cast<const uint4*>(base + o);
-      av[j][1] = *reinterpret_cast<const uint4*>(base + o + static_cast<uint32_t>(cd) * 16);
-    }
+    for (int j = 0; j < 8; ++j) load_group(j, soff);
   };
 
   // rows of the lane's row groups whose position is outside the table (bit j)
   uint32_t bad_rows = 0;
   const int R = p.R;
   const int half = R >> 1;
-  // is the stage at element offset `col` of group g the last 128 dims of a head?
-  auto rope_stage = [&](int kb) __attribute__((always_inline)) {
-    if constexpr (!ROPE) return false;
-    const int colg = g * p.K + real_stage(kb) * kBK;
-    return (colg + kBK) % p.D == 0;
-  };
+  // bit kb: loop stage kb holds the last 128 dims of a head (the rotated
+  // slice).  Taken once per tile into a scalar register, so that the choice
+  // of rotating code per stage is a uniform branch.
+  uint32_t rope_bits = 0;
+  if constexpr (ROPE) {
+    for (int kb = 0; kb < KB; ++kb) {
+      const int colg = g * p.K + real_stage(kb) * kBK;
+      rope_bits |= ((colg + kBK) % p.D == 0 ? 1u : 0u) << kb;
+    }
+    rope_bits = __builtin_amdgcn_readfirstlane(rope_bits);
+  }
+  auto rope_stage = [&](int kb) __attribute__((always_inline)) { return ROPE && ((rope_bits >> kb) & 1u); };
 
   // ---- quantise the stage in av[] into buffer `buf` (A region) and asc[sb]
   // LDS byte offsets of the lane's two 8-byte code pieces in row group 0:
@@ -257,10 +312,8 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int szr = swz8(ri);
   auto piece_off = [&](int ch, int sz) __attribute__((always_inline)) { return (((ch >> 1) ^ sz) << 4) + (ch & 1) * 8; };
   const uint32_t qoff[2][2] = {
-      {static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr)),
-       static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(ca, szr ^ 4))},
-      {static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(cb, szr)),
-       static_cast<uint32_t>(kOpBytes + arow0 * kBK + piece_off(cb, szr ^ 4))}};
+      {static_cast<uint32_t>(arow0 * kBK + piece_off(ca, szr)), static_cast<uint32_t>(arow0 * kBK + piece_off(ca, szr ^ 4))},
+      {static_cast<uint32_t>(arow0 * kBK + piece_off(cb, szr)), static_cast<uint32_t>(arow0 * kBK + piece_off(cb, szr ^ 4))}};
   // asc byte of tile row tr = 64 wave + ri + 8j: [tr / 128][tr % 32][(tr / 32) % 4]
   const int sc_lane = (wave >> 1) * 128 + ri * 4;
   // ---- rotation tables of a rope stage: the cos and sin rows of the tile's
@@ -271,9 +324,9 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // rotation has read its tables, so no barrier is involved.  8 DMA
   // instructions per wave: 8 lanes (16-byte pieces) per row, 8 rows each;
   // pieces past the 2R bytes re-read the first (never used).
-  auto issue_cs = [&](uint8_t* buf, int kb) __attribute__((always_inline)) {
+  auto issue_cs = [&](uint8_t* ba, int kb) __attribute__((always_inline)) {
     if (!ROPE || !rope_stage(kb)) return;
-    uint8_t* dst = buf + kOpBytes + wave * 64 * kBK;
+    uint8_t* dst = ba + wave * 64 * kBK;
     const int piece = lane & 7;
     const int npc = R >> 4;                          // 16-byte pieces per table row
 #pragma unroll
@@ -296,6 +349,18 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const bool rot_b = NEOX ? ca >= first_rot : cb >= first_rot;
   const int ti_a = NEOX ? (rot_a ? (ca - first_rot) * 8 : 0) : (rot_a ? (ca - first_rot) * 4 : 0);
   const int ti_b = NEOX ? ti_a : (rot_b ? (cb - first_rot) * 4 : 0);
+  // all-ones where the chunk is rotated: the rotated value is blended in
+  // with these (opaque to the compiler, which otherwise turned the choice
+  // into divergent branches around the rotation)
+  uint32_t rmask_a = rot_a ? ~0u : 0u, rmask_b = rot_b ? ~0u : 0u;
+  asm volatile("" : "+v"(rmask_a), "+v"(rmask_b));
+  auto blend = [](uint4 v, const uint4 r, uint32_t msk) __attribute__((always_inline)) {
+    v.x = (r.x & msk) | (v.x & ~msk);
+    v.y = (r.y & msk) | (v.y & ~msk);
+    v.z = (r.z & msk) | (v.z & ~msk);
+    v.w = (r.w & msk) | (v.w & ~msk);
+    return v;
+  };
   auto rotate2 = [&](const uint8_t* tab, uint4& v0, uint4& v1) __attribute__((always_inline)) {
     const uint16_t* crow = reinterpret_cast<const uint16_t*>(tab);
     const uint16_t* srow = crow + half;
@@ -314,12 +379,12 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
         r.w = pk_bf16(xr, yr);
         return r;
       };
-      const uint4 ra = rot_chunk(v0, *reinterpret_cast<const uint2*>(crow + ti_a),
-                                 *reinterpret_cast<const uint2*>(srow + ti_a));
+      // a lane's first chunk (ca = c < 8) lies before the rotated slice,
+      // which starts at chunk (128 - R) / 8 >= 8 for R <= 64: only the
+      // second chunk can be rotated
       const uint4 rb = rot_chunk(v1, *reinterpret_cast<const uint2*>(crow + ti_b),
                                  *reinterpret_cast<const uint2*>(srow + ti_b));
-      if (rot_a) v0 = ra;
-      if (rot_b) v1 = rb;
+      v1 = blend(v1, rb, rmask_b);
     } else {
       // pairs (i, i + R/2): chunk ca holds x of pairs i0 .. i0+7, chunk cb their y
       const uint4 cc = *reinterpret_cast<const uint4*>(crow + ti_a);
@@ -337,47 +402,54 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
         xo[k] = pk_bf16(x0, x1);
         yo[k] = pk_bf16(y0, y1);
       }
-      if (rot_a) {
-        v0 = make_uint4(xo[0], xo[1], xo[2], xo[3]);
-        v1 = make_uint4(yo[0], yo[1], yo[2], yo[3]);
-      }
+      v0 = blend(v0, make_uint4(xo[0], xo[1], xo[2], xo[3]), rmask_a);
+      v1 = blend(v1, make_uint4(yo[0], yo[1], yo[2], yo[3]), rmask_a);
     }
   };
 
-  // quantise stage kb from av[]: `rot` rotates it first (a rope stage); the
-  // two versions are separate code, chosen per stage, so that the rotation's
-  // registers are needed only in the stages that rotate
-  auto quantise_v = [&](auto rot, uint8_t* buf, int sb) __attribute__((always_inline)) {
-    constexpr bool RS = decltype(rot)::value;
-    const uint8_t* tab = buf + kOpBytes + arow0 * kBK;   // row group 0's tables (rope stage)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      uint4 v0 = av[j][0], v1 = av[j][1];
-      if constexpr (RS) rotate2(tab + j * 8 * kBK, v0, v1);
-      uint32_t m = max(amax_bits8(v0), amax_bits8(v1));
-      if (ROPE && ((bad_rows >> j) & 1)) m = 0x7F80u;   // position outside the table: NaN scale
-      m = max8(m);
-      const bool finite = m < 0x7F80u;
-      const int e = e8m0_exponent<8>(finite ? m : 0);
-      const float sbits = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
-      uint2 q0 = encode8(v0, sbits), q1 = encode8(v1, sbits);
-      if (!finite) q0 = q1 = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      uint32_t o0 = qoff[0][j & 1], o1 = qoff[1][j & 1];
-      asm volatile("" : "+v"(o0), "+v"(o1));        // not hoisted per row group
-      *reinterpret_cast<uint2*>(buf + o0 + j * 8 * kBK) = q0;
-      *reinterpret_cast<uint2*>(buf + o1 + j * 8 * kBK) = q1;
-      if (c == 0)
-        (&asc[sb][0][0][0])[sc_lane + (j & 3) * 32 + ((2 * wave + (j >> 2)) & 3)] =
-            static_cast<uint8_t>(finite ? e + 127 : 0xFF);
-      // one row group's temporaries at a time
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  // quantise row group j of the stage in av[] into buffer `buf` (A region)
+  // and asc[sb], rotating it first if `rs` (a rope stage; a uniform branch
+  // around the rotation alone, so that no MFMA is on either side of it).
+  // The 8 lanes of a row hold the same scale byte and all of them store it.
+  // `between(k)`, k = 0..3, runs at four fixed points of the work (the
+  // stage loop puts one MFMA there); the order is pinned by scheduling
+  // barriers, so that each MFMA runs beside the vector work after it.
+  // (The waits for the group's loads and, in a rope stage, its table DMA are
+  // the compiler's: it waits before the first use of a loaded register or of
+  // LDS that an outstanding DMA may write.)
+  auto quant_group = [&](bool rs, auto jc, uint8_t* ba, int sb, auto&& between) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    uint4 v0 = av[j][0], v1 = av[j][1];
+    if (ROPE && rs) rotate2(ba + (arow0 + 8 * j) * kBK, v0, v1);
+    uint32_t m = max(amax_bits8(v0), amax_bits8(v1));
+    if (ROPE && ((bad_rows >> j) & 1)) m = 0x7F80u;   // position outside the table: NaN scale
+    between(ic<0>{});
+    m = max8(m);
+    const bool finite = m < 0x7F80u;
+    const int e = e8m0_exponent<8>(finite ? m : 0);
+    const float sbits = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    between(ic<1>{});
+    uint2 q0 = encode8(v0, sbits), q1 = encode8(v1, sbits);
+    // a non-finite group: codes 0x7F (a blend with an opaque mask, which the
+    // compiler does not turn into a branch)
+    uint32_t fin = finite ? ~0u : 0u;
+    asm volatile("" : "+v"(fin));
+    q0.x = (q0.x & fin) | (0x7F7F7F7Fu & ~fin);
+    q0.y = (q0.y & fin) | (0x7F7F7F7Fu & ~fin);
+    q1.x = (q1.x & fin) | (0x7F7F7F7Fu & ~fin);
+    q1.y = (q1.y & fin) | (0x7F7F7F7Fu & ~fin);
+    between(ic<2>{});
+    *reinterpret_cast<uint2*>(ba + qoff[0][j & 1] + j * 8 * kBK) = q0;
+    *reinterpret_cast<uint2*>(ba + qoff[1][j & 1] + j * 8 * kBK) = q1;
+    (&asc[sb][0][0][0])[sc_lane + (j & 3) * 32 + ((2 * wave + (j >> 2)) & 3)] =
+        static_cast<uint8_t>(finite ? e + 127 : 0xFF);
+    between(ic<3>{});
   };
-  auto quantise = [&](int kb, uint8_t* buf, int sb) __attribute__((always_inline)) {
-    if (ROPE && rope_stage(kb))
-      quantise_v(std::true_type{}, buf, sb);
-    else
-      quantise_v(std::false_type{}, buf, sb);
+  auto quantise = [&](int kb, uint8_t* ba, int sb) __attribute__((always_inline)) {
+    const bool rs = rope_stage(kb);
+    auto g8 = [&](auto jc) __attribute__((always_inline)) { quant_group(rs, jc, ba, sb, [](auto) {}); };
+    g8(ic<0>{}); g8(ic<1>{}); g8(ic<2>{}); g8(ic<3>{});
+    g8(ic<4>{}); g8(ic<5>{}); g8(ic<6>{}); g8(ic<7>{});
   };
 
   // ---- fragments (as bmm_large_kernel): row wn*128 + 32i + lane%32 of W,
@@ -386,7 +458,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   const int r32 = lane & 31;
   const int q2 = lane >> 5;
   const int rdW = (wn * 128 + r32) * kBK;
-  const int rdA = kOpBytes + (wt * 128 + r32) * kBK;
+  const int rdA = (wt * 128 + r32) * kBK;
   const int sz = swz8(r32);
   const int ch0[2] = {(q2 ^ sz) << 4, ((4 + q2) ^ sz) << 4};
   const int ch1[2] = {((q2 + 2) ^ sz) << 4, ((6 + q2) ^ sz) << 4};
@@ -402,27 +474,65 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto mma_stage = [&](const uint8_t* buf, int kb, int sb) __attribute__((always_inline)) {
+  // One stage: the 32 MFMAs of stage kb (two K-halves of fragments, 64
+  // VGPRs each, the second read when the first half's MFMAs are issued).
+  // MODE 1 and 2 quantise stage kb+1 (av[] into `na`) alongside them: the
+  // first kPure MFMAs run alone, then each row group goes with kPerGroup
+  // MFMAs placed at fixed points of its work (scheduling barriers and opaque
+  // accumulator copies pin the order, so each MFMA runs beside the vector
+  // work after it).  The first use of av[] waits for every load and DMA in
+  // flight -- the compiler's rule while LDS-DMA is outstanding -- so the MFMAs
+  // before it give the previous iteration's weight DMA that much more time.
+  // MODE 2 also reloads each row group's registers with stage kb+2's BF16 as
+  // soon as they are free.
+  auto step = [&](auto mode, const uint8_t* cw, const uint8_t* ca, uint8_t* na, int kb) __attribute__((always_inline)) {
+    constexpr int MODE = decltype(mode)::value;
     const uint32_t swv = *reinterpret_cast<const uint32_t*>(&wsc[real_stage(kb)][wn][r32][0]);
-    const uint32_t sav = *reinterpret_cast<const uint32_t*>(&asc[sb][wt][r32][0]);
+    const uint32_t sav = *reinterpret_cast<const uint32_t*>(&asc[kb & 1][wt][r32][0]);
+    const bool rs = MODE >= 1 && rope_stage(kb + 1);
+    const uint32_t nb = MODE == 2 ? stage_soff(kb + 2) : 0u;
+    v8i fw[4], fa[4];
+    auto read_half = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      // one half's fragments at a time (64 VGPRs): the BF16 of the next
-      // stage is held in registers meanwhile
-      __builtin_amdgcn_sched_barrier(0);
-      v8i fw[4], fa[4];
+      for (int i = 0; i < 4; ++i) fw[i] = read_frag(cw + rdW + i * 32 * kBK, h);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fw[i] = read_frag(buf + rdW + i * 32 * kBK, h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fa[j] = read_frag(buf + rdA + j * 32 * kBK, h);
-      mfma_all(acc, fw, fa, swv, sav);
-      // the MFMAs are pure: without a use here the compiler sinks them below
-      // the quantisation that follows, keeping their fragments live across it
+      for (int j = 0; j < 4; ++j) fa[j] = read_frag(ca + rdA + j * 32 * kBK, h);
+    };
+    auto pin_all = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+    };
+    auto mfma_at = [&](auto mc) __attribute__((always_inline)) {   // MFMA m of the stage
+      constexpr int m = decltype(mc)::value, K = m % 16;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (m == 16) {
+        pin_all();
+        read_half(1);
+      }
+      asm volatile("" : "+a"(acc[K / 4][K % 4]));
+      mfma_range<K, K + 1>(acc, fw, fa, swv, sav);
+      asm volatile("" : "+a"(acc[K / 4][K % 4]));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_half(0);
+    if constexpr (MODE == 0) {
+      static_for<0, 32>(mfma_at);
+    } else {
+      static_for<0, kPure>(mfma_at);
+      static_for<0, 8>([&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        quant_group(rs, gc, na, (kb + 1) & 1, [&](auto kc) __attribute__((always_inline)) {
+          static_for<0, kPerGroup>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            if constexpr (hook_of(kPerGroup, q) == decltype(kc)::value) mfma_at(ic<kPure + g * kPerGroup + q>{});
+          });
+        });
+        if constexpr (MODE == 2) load_group(g, nb);
+      });
     }
+    pin_all();
     __builtin_amdgcn_sched_barrier(0);
   };
 
@@ -443,15 +553,15 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     for (int j = 0; j < 8; ++j) bad_rows |= (spos[arow0 + 8 * j] < 0 ? 1u : 0u) << j;
   }
   load_a(0);
-  issue_cs(st0, 0);
-  issue_w(st0, 0);
+  issue_cs(sa0, 0);
+  issue_w(sw0, 0);
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
   stage_barrier();
-  quantise(0, st0, 0);
+  quantise(0, sa0, 0);
   if (KB > 1) {                                      // stage 1 into the unused buffer
     load_a(1);
-    issue_cs(st1, 1);
-    issue_w(st1, 1);
+    issue_cs(sa1, 1);
+    issue_w(sw1, 1);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmMax);
   stage_barrier();                                   // stage 0's codes are in st0
@@ -459,33 +569,42 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // ---- stage loop.  On entry to iteration kb: buffer kb%2 holds stage kb
   // (W and the quantised A); this wave's loads of stage kb+1's BF16, its
   // rotation tables and then the DMA of its W (into the other buffer) may be
-  // in flight.  (The prologue above is outside the loop, and every lambda is
-  // inlined: with a first iteration that skipped the MFMAs, or with the
-  // quantiser as a called function, the register allocator moved the
-  // accumulators through scratch memory on every stage.)
-  for (int kb = 0; kb < KB; ++kb) {
-    uint8_t* cur = (kb & 1) ? st1 : st0;
-    uint8_t* nxt = (kb & 1) ? st0 : st1;
-    const bool more = kb + 1 < KB;
-    // stage kb+1's BF16 and tables have landed once at most its W DMA is pending
-    if (more) __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
-    mma_stage(cur, kb, kb & 1);
-    if (more) {
-      quantise(kb + 1, nxt, (kb + 1) & 1);
-      if (kb + 2 < KB) {
-        load_a(kb + 2);
-        // stage kb+1's W has landed once at most stage kb+2's loads are pending
-        __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
-      } else {
-        __builtin_amdgcn_s_waitcnt(wait_vm(0));
-      }
-    }
-    stage_barrier();                                 // everyone is done with `cur`; stage kb+1 is in `nxt`
-    if (kb + 2 < KB) {
-      issue_cs(cur, kb + 2);
-      issue_w(cur, kb + 2);
-    }
+  // in flight.  The last two stages are peeled (no reload, then no
+  // quantisation).  (Every lambda is inlined and no iteration skips the
+  // MFMAs: with a first iteration that did, or with the quantiser as a
+  // called function, the register allocator moved the accumulators through
+  // scratch memory on every stage.)
+  // One loop iteration with its buffers named: kb even reads st0 and fills
+  // st1, kb odd the reverse.  With the buffers fixed per call (the loop runs
+  // two stages per trip) the compiler can tell the fragment reads from the
+  // DMA into the other buffer; with a run-time choice it made every stage
+  // wait for all outstanding loads first.
+  auto iter = [&](uint8_t* cw, uint8_t* ca, uint8_t* na, int kb) __attribute__((always_inline)) {
+    step(ic<2>{}, cw, ca, na, kb);
+    // stage kb+1's W has landed once at most stage kb+2's loads are pending
+    __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
+    stage_barrier();                                 // everyone is done with stage kb's buffers; stage kb+1 is in the other
+    issue_cs(ca, kb + 2);
+    issue_w(cw, kb + 2);
+  };
+  int kb = 0;
+  for (; kb + 3 < KB; kb += 2) {
+    iter(sw0, sa0, sa1, kb);
+    iter(sw1, sa1, sa0, kb + 1);
   }
+  if (kb + 2 < KB) {                                 // kb even
+    iter(sw0, sa0, sa1, kb);
+    ++kb;
+  }
+  if (kb + 1 < KB) {                                 // kb = KB - 2
+    // stage kb+1's BF16 and tables have landed once at most its W DMA is pending
+    __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
+    step(ic<1>{}, (kb & 1) ? sw1 : sw0, (kb & 1) ? sa1 : sa0, (kb & 1) ? sa0 : sa1, kb);
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    stage_barrier();
+    ++kb;
+  }
+  step(ic<0>{}, (kb & 1) ? sw1 : sw0, (kb & 1) ? sa1 : sa0, nullptr, kb);   // kb = KB - 1
   __builtin_amdgcn_s_waitcnt(wait_vm(0));          // no DMA outlives the workgroup
 
   // ---- epilogue straight from the accumulators (as bmm_large_kernel)
