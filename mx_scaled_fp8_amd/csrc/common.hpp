@@ -74,8 +74,10 @@ inline DivU32 make_div(uint32_t d) {
 // not waited on.  kWaitLgkmOnly: LDS/scalar memory only.
 constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4); }
 constexpr int kWaitLgkmOnly = wait_vm(63) | 0xF;
+// at most n vector-memory instructions outstanding; LDS and scalar memory not waited on
+constexpr int wait_vm_only(int n) { return wait_vm(n) | 0x0F00; }
 static_assert(wait_vm(0) == 0x0070 && wait_vm(16) == 0x4070 && wait_vm(18) == 0x4072 && wait_vm(24) == 0x4078 &&
-                  wait_vm(32) == 0x8070 && kWaitLgkmOnly == 0xC07F,
+                  wait_vm(32) == 0x8070 && kWaitLgkmOnly == 0xC07F && wait_vm_only(8) == 0x0F78,
               "s_waitcnt encoding");
 
 __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 dv) {

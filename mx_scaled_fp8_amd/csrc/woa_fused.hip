@@ -57,12 +57,11 @@ constexpr int kOpBytes = kTile * kBK;       // 32 KiB per operand per stage
 constexpr int kMaxKB = 32;                  // K <= 4096: the W scales of a tile stay in LDS
 constexpr int kFmtFp8 = 0;
 
-// vector-memory instructions a wave issues per stage (the waits below count them)
-constexpr int kALoadsPerStage = 16;         // 8 row groups x 2 chunks
-constexpr int kWDmaPerStage = kTile / 32;   // 8 row groups of 32 rows, one DMA instruction each
+#ifndef WOA_WAVES
+#define WOA_WAVES 8
+#endif
 
 constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
-static_assert(kALoadsPerStage == 8 * 2 && kWDmaPerStage == 8, "instructions per stage");
 template <int N>
 using ic = std::integral_constant<int, N>;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
@@ -75,15 +74,7 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-// Of the 32 MFMAs of a stage, the first kPure run before any quantisation
-// work and the rest go kPerGroup to a row group; MFMA q of a row group is
-// issued at point hook_of(kPerGroup, q) (0..3) of the group's work.
-#ifndef WOA_PURE_MFMAS
-#define WOA_PURE_MFMAS 16
-#endif
-constexpr int kPure = WOA_PURE_MFMAS;
-constexpr int kPerGroup = (32 - kPure) / 8;
-static_assert(kPure % 8 == 0 && kPerGroup >= 1 && kPerGroup <= 4, "MFMAs per row group");
+// MFMA q (0, 1) of a row group is issued at point 2q (0..3) of the group's work
 constexpr int hook_of(int per_group, int q) { return per_group == 2 ? 2 * q : q; }
 
 struct FusedArgs {
@@ -166,35 +157,37 @@ __device__ __forceinline__ uint2 encode8(const uint4 v, float sbits) {
   return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-// W tile I times A tile J; the scale operands are 4-byte words holding the
-// scales of tiles 0..3 and the byte selects pick tile I's and J's
-template <int I, int J>
-__device__ __forceinline__ void mfma_ij(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+// W tile I times A tile J (of the wave's NJ); the scale operands are 4-byte
+// words holding the scales of the wave's tiles and the byte selects pick
+// tile I's and J's
+template <int I, int J, int NJ>
+__device__ __forceinline__ void mfma_ij(v16f (&acc)[4][NJ], const v8i (&w)[4], const v8i (&a)[NJ], uint32_t swv,
                                         uint32_t sav) {
   acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w[I], a[J], acc[I][J], kFmtFp8, kFmtFp8, I,
                                                              static_cast<int>(swv), J, static_cast<int>(sav));
 }
 
-template <int IJ, int END>
-__device__ __forceinline__ void mfma_range(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
+template <int IJ, int END, int NJ>
+__device__ __forceinline__ void mfma_range(v16f (&acc)[4][NJ], const v8i (&w)[4], const v8i (&a)[NJ], uint32_t swv,
                                            uint32_t sav) {
   if constexpr (IJ < END) {
-    mfma_ij<IJ / 4, IJ % 4>(acc, w, a, swv, sav);
-    mfma_range<IJ + 1, END>(acc, w, a, swv, sav);
+    mfma_ij<IJ / NJ, IJ % NJ, NJ>(acc, w, a, swv, sav);
+    mfma_range<IJ + 1, END, NJ>(acc, w, a, swv, sav);
   }
 }
 
-template <int IJ = 0>
-__device__ __forceinline__ void mfma_all(v16f (&acc)[4][4], const v8i (&w)[4], const v8i (&a)[4], uint32_t swv,
-                                         uint32_t sav) {
-  if constexpr (IJ < 16) {
-    mfma_ij<IJ / 4, IJ % 4>(acc, w, a, swv, sav);
-    mfma_all<IJ + 1>(acc, w, a, swv, sav);
-  }
-}
-
-template <bool ROPE, bool NEOX>
-__global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
+template <int NW, bool ROPE, bool NEOX>
+__global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int NJ = NW == 4 ? 4 : 2;              // A tiles of 32 rows per wave (W tiles: 4)
+  constexpr int kRowsPerWave = kTile / NW;         // rows a wave quantises: 64 or 32
+  constexpr int NG = kRowsPerWave / 8;             // its row groups of 8 rows
+  constexpr int kWDma = kTile / (8 * NW);          // W DMA instructions per wave and stage
+  constexpr int kALoads = 2 * NG;                  // A loads per wave and stage
+  constexpr int kMfmas = 8 * NJ;                   // MFMAs per wave and stage (two K-halves)
+  constexpr int kPure = kMfmas / 2;                // MFMAs of a stage before its quantisation work
+  constexpr int kPerGroup = (kMfmas - kPure) / NG; // MFMAs with each row group
+  static_assert(kPerGroup == 2, "two MFMAs per row group");
   // stage buffers 0 and 1: W tile 256 x 128 B (sw) and A tile 256 x 128 B
   // (sa), four separate arrays so that the compiler can tell the weight DMA
   // from the activation codes and tables (with one array per stage it made
@@ -205,8 +198,8 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[kOpBytes];
   // W scales of every stage of the tile, [stage][wave half][row % 32][tile]
   __shared__ __attribute__((aligned(16))) uint8_t wsc[kMaxKB][2][32][4];
-  // A scales of the stage in each buffer, [buffer][wave half][row % 32][tile]
-  __shared__ __attribute__((aligned(16))) uint8_t asc[2][2][32][4];
+  // A scales of the stage in each buffer, [buffer][wave row wt][row % 32][tile j < NJ]
+  __shared__ __attribute__((aligned(16))) uint8_t asc[2][4][32][4];
   // positions of the tile's rows (-1: outside the table)
   __shared__ int32_t spos[kTile];
 
@@ -241,22 +234,23 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   auto issue_w = [&](uint8_t* bw, int kb) __attribute__((always_inline)) {
     const uint8_t* bW = baseW + static_cast<uint32_t>(real_stage(kb)) * kBK;
 #pragma unroll
-    for (int it = 0; it < kWDmaPerStage; ++it) {
+    for (int it = 0; it < kWDma; ++it) {
       uint32_t b = offW0;
       asm volatile("" : "+v"(b));                    // formed per issue, not held as 8 addresses
-      const uint32_t o = min(b + static_cast<uint32_t>(it * 32) * static_cast<uint32_t>(p.K), capW);
-      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(bw + (it * 32 + wave * 8) * kBK), 16, 0, 0);
+      const uint32_t o = min(b + static_cast<uint32_t>(it * 8 * NW) * static_cast<uint32_t>(p.K), capW);
+      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(bw + (it * 8 * NW + wave * 8) * kBK), 16, 0, 0);
     }
   };
 
   // ---- A: lane (row ri = lane / 8 of a group of 8 rows, c = lane % 8)
   // holds chunks ca and ca + cd of the row's 16 chunks of 8 BF16; wave w
-  // owns tile rows 64w .. 64w + 63 (row group j: rows 64w + 8j + ri)
+  // quantises tile rows R w .. R w + R - 1, R = kRowsPerWave (row group j:
+  // rows R w + 8j + ri)
   const int ri = lane >> 3, c = lane & 7;
   const int cd = p.cd;
   const int ca = (c / cd) * 2 * cd + (c % cd);
   const int cb = ca + cd;
-  const int arow0 = wave * 64 + ri;               // tile row of row group 0
+  const int arow0 = wave * kRowsPerWave + ri;     // tile row of row group 0
   // A goes through a buffer resource whose base is the tile's first row
   // (group g's columns) and whose size ends at row T: rows past T read
   // zeros (their outputs are never stored).  A lane's two offsets are fixed
@@ -270,11 +264,11 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
       static_cast<int>(min(valid_bytes, static_cast<uint64_t>(0xFFFFFFFFu))), kBufferFlags);
   const uint32_t voff_a = static_cast<uint32_t>(arow0) * row_bytes + static_cast<uint32_t>(ca) * 16;
   const uint32_t voff_b = voff_a + static_cast<uint32_t>(cd) * 16;
-  uint4 av[8][2];
+  uint4 av[NG][2];
   auto stage_soff = [&](int kb) __attribute__((always_inline)) {
     return static_cast<uint32_t>(real_stage(kb)) * (2 * kBK);
   };
-  // row group j (rows 64 wave + 8j + ri) of the stage at scalar offset soff into av[j]
+  // row group j of the stage at scalar offset soff into av[j]
   auto load_group = [&](int j, uint32_t soff) __attribute__((always_inline)) {
     const uint32_t so = soff + static_cast<uint32_t>(8 * j) * row_bytes;
     const v4u a0 = __builtin_amdgcn_raw_buffer_load_b128(xres, static_cast<int>(voff_a), static_cast<int>(so), 0);
@@ -285,7 +279,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   auto load_a = [&](int kb) __attribute__((always_inline)) {
     const uint32_t soff = stage_soff(kb);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) load_group(j, soff);
+    for (int j = 0; j < NG; ++j) load_group(j, soff);
   };
 
   // rows of the lane's row groups whose position is outside the table (bit j)
@@ -308,30 +302,35 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // ---- quantise the stage in av[] into buffer `buf` (A region) and asc[sb]
   // LDS byte offsets of the lane's two 8-byte code pieces in row group 0:
   // row tr = arow0 + 8j is at + 1024 j, and its swizzle swz8(tr) depends on
-  // tr % 16 only, so it is swz8(ri) for even j and swz8(ri) ^ 4 for odd j
+  // tr % 16 only (kRowsPerWave is a multiple of 16), so it is swz8(ri) for
+  // even j and swz8(ri) ^ 4 for odd j
   const int szr = swz8(ri);
   auto piece_off = [&](int ch, int sz) __attribute__((always_inline)) { return (((ch >> 1) ^ sz) << 4) + (ch & 1) * 8; };
   const uint32_t qoff[2][2] = {
       {static_cast<uint32_t>(arow0 * kBK + piece_off(ca, szr)), static_cast<uint32_t>(arow0 * kBK + piece_off(ca, szr ^ 4))},
       {static_cast<uint32_t>(arow0 * kBK + piece_off(cb, szr)), static_cast<uint32_t>(arow0 * kBK + piece_off(cb, szr ^ 4))}};
-  // asc byte of tile row tr = 64 wave + ri + 8j: [tr / 128][tr % 32][(tr / 32) % 4]
-  const int sc_lane = (wave >> 1) * 128 + ri * 4;
+  // asc byte of tile row tr = arow0 + 8j (A tile tr / 32 = wave R / 32 + j / 4
+  // is tile (tr / 32) % NJ of wave row (tr / 32) / NJ): [wave row][tr % 32][tile]
+  auto sc_index = [&](int j) __attribute__((always_inline)) {
+    const int blk = wave * (kRowsPerWave / 32) + (j >> 2);
+    return (blk / NJ) * 128 + (8 * (j & 3) + ri) * 4 + blk % NJ;
+  };
   // ---- rotation tables of a rope stage: the cos and sin rows of the tile's
   // tokens go by LDS-DMA into the A region of the stage's buffer (free until
   // the stage's codes are written there), each at the 128 bytes its token's
   // codes will take: cos[R/2] then sin[R/2] (R <= 64).  A wave loads and
-  // reads only its own 64 rows, and a row's codes are written after its
-  // rotation has read its tables, so no barrier is involved.  8 DMA
-  // instructions per wave: 8 lanes (16-byte pieces) per row, 8 rows each;
+  // reads only its own rows, and a row's codes are written after its
+  // rotation has read its tables, so no barrier is involved.  One DMA
+  // instruction per row group: 8 lanes (16-byte pieces) per row, 8 rows;
   // pieces past the 2R bytes re-read the first (never used).
   auto issue_cs = [&](uint8_t* ba, int kb) __attribute__((always_inline)) {
     if (!ROPE || !rope_stage(kb)) return;
-    uint8_t* dst = ba + wave * 64 * kBK;
+    uint8_t* dst = ba + wave * kRowsPerWave * kBK;
     const int piece = lane & 7;
     const int npc = R >> 4;                          // 16-byte pieces per table row
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int tr = wave * 64 + k * 8 + (lane >> 3);      // tile row
+    for (int k = 0; k < NG; ++k) {
+      int tr = wave * kRowsPerWave + k * 8 + (lane >> 3);   // tile row
       asm volatile("" : "+v"(tr));                   // read here, not hoisted as 8 live positions and pointers
       const int pj = max(spos[tr], 0);               // outside the table: row 0 (its codes are NaN)
       const uint16_t* src = piece < npc ? p.cos + static_cast<int64_t>(pj) * half + piece * 8
@@ -414,13 +413,19 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   // `between(k)`, k = 0..3, runs at four fixed points of the work (the
   // stage loop puts one MFMA there); the order is pinned by scheduling
   // barriers, so that each MFMA runs beside the vector work after it.
-  // (The waits for the group's loads and, in a rope stage, its table DMA are
-  // the compiler's: it waits before the first use of a loaded register or of
-  // LDS that an outstanding DMA may write.)
-  auto quant_group = [&](bool rs, auto jc, uint8_t* ba, int sb, auto&& between) __attribute__((always_inline)) {
+  // The waits for the group's loads are the compiler's (before the first
+  // use of a loaded register).  The table DMA of a rope stage is waited for
+  // here, before the first group rotates: `tab_wait` is the number of
+  // vector-memory instructions this wave issued after it (0: already waited).
+  auto quant_group = [&](bool rs, auto jc, uint8_t* ba, int sb, auto tab_wait, auto&& between)
+                         __attribute__((always_inline)) {
     constexpr int j = decltype(jc)::value;
     uint4 v0 = av[j][0], v1 = av[j][1];
-    if (ROPE && rs) rotate2(ba + (arow0 + 8 * j) * kBK, v0, v1);
+    if (ROPE && rs) {
+      if constexpr (j == 0 && decltype(tab_wait)::value > 0)
+        __builtin_amdgcn_s_waitcnt(wait_vm_only(decltype(tab_wait)::value));
+      rotate2(ba + (arow0 + 8 * j) * kBK, v0, v1);
+    }
     uint32_t m = max(amax_bits8(v0), amax_bits8(v1));
     if (ROPE && ((bad_rows >> j) & 1)) m = 0x7F80u;   // position outside the table: NaN scale
     between(ic<0>{});
@@ -441,24 +446,21 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     between(ic<2>{});
     *reinterpret_cast<uint2*>(ba + qoff[0][j & 1] + j * 8 * kBK) = q0;
     *reinterpret_cast<uint2*>(ba + qoff[1][j & 1] + j * 8 * kBK) = q1;
-    (&asc[sb][0][0][0])[sc_lane + (j & 3) * 32 + ((2 * wave + (j >> 2)) & 3)] =
-        static_cast<uint8_t>(finite ? e + 127 : 0xFF);
+    (&asc[sb][0][0][0])[sc_index(j)] = static_cast<uint8_t>(finite ? e + 127 : 0xFF);
     between(ic<3>{});
   };
   auto quantise = [&](int kb, uint8_t* ba, int sb) __attribute__((always_inline)) {
     const bool rs = rope_stage(kb);
-    auto g8 = [&](auto jc) __attribute__((always_inline)) { quant_group(rs, jc, ba, sb, [](auto) {}); };
-    g8(ic<0>{}); g8(ic<1>{}); g8(ic<2>{}); g8(ic<3>{});
-    g8(ic<4>{}); g8(ic<5>{}); g8(ic<6>{}); g8(ic<7>{});
+    static_for<0, NG>([&](auto jc) __attribute__((always_inline)) { quant_group(rs, jc, ba, sb, ic<0>{}, [](auto) {}); });
   };
 
   // ---- fragments (as bmm_large_kernel): row wn*128 + 32i + lane%32 of W,
-  // wt*128 + 32j + lane%32 of A; lane group q2 takes logical chunks 4h + q2
+  // wt*32*NJ + 32j + lane%32 of A; lane group q2 takes logical chunks 4h + q2
   // and 4h + q2 + 2 of 64-K half h
   const int r32 = lane & 31;
   const int q2 = lane >> 5;
   const int rdW = (wn * 128 + r32) * kBK;
-  const int rdA = (wt * 128 + r32) * kBK;
+  const int rdA = (wt * 32 * NJ + r32) * kBK;
   const int sz = swz8(r32);
   const int ch0[2] = {(q2 ^ sz) << 4, ((4 + q2) ^ sz) << 4};
   const int ch1[2] = {((q2 + 2) ^ sz) << 4, ((6 + q2) ^ sz) << 4};
@@ -466,16 +468,16 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     return make_v8i(*reinterpret_cast<const uint4*>(q + ch0[h]), *reinterpret_cast<const uint4*>(q + ch1[h]));
   };
 
-  v16f acc[4][4];
+  v16f acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // One stage: the 32 MFMAs of stage kb (two K-halves of fragments, 64
-  // VGPRs each, the second read when the first half's MFMAs are issued).
+  // One stage: the kMfmas MFMAs of stage kb (two K-halves of fragments, the
+  // second read when the first half's MFMAs are issued).
   // MODE 1 and 2 quantise stage kb+1 (av[] into `na`) alongside them: the
   // first kPure MFMAs run alone, then each row group goes with kPerGroup
   // MFMAs placed at fixed points of its work (scheduling barriers and opaque
@@ -491,39 +493,49 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
     const uint32_t sav = *reinterpret_cast<const uint32_t*>(&asc[kb & 1][wt][r32][0]);
     const bool rs = MODE >= 1 && rope_stage(kb + 1);
     const uint32_t nb = MODE == 2 ? stage_soff(kb + 2) : 0u;
-    v8i fw[4], fa[4];
-    auto read_half = [&](int h) __attribute__((always_inline)) {
+    v8i fw[4], fa[NJ];
+    auto read_w = [&](int i, int h) __attribute__((always_inline)) { fw[i] = read_frag(cw + rdW + i * 32 * kBK, h); };
+    auto read_a = [&](int h) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fw[i] = read_frag(cw + rdW + i * 32 * kBK, h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) fa[j] = read_frag(ca + rdA + j * 32 * kBK, h);
+      for (int j = 0; j < NJ; ++j) fa[j] = read_frag(ca + rdA + j * 32 * kBK, h);
     };
     auto pin_all = [&]() __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
     };
     auto mfma_at = [&](auto mc) __attribute__((always_inline)) {   // MFMA m of the stage
-      constexpr int m = decltype(mc)::value, K = m % 16;
+      constexpr int m = decltype(mc)::value, K = m % (4 * NJ), I = K / NJ;
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (m == 16) {
+      // the second half's fragments: A and W tiles 0 and 1 at its first MFMA,
+      // then W tile I + 1 at the first MFMA of W tile I (two W tiles live at
+      // a time, while the quantisation runs beside these MFMAs)
+      if constexpr (m == 4 * NJ) {
         pin_all();
-        read_half(1);
+        read_a(1);
+        read_w(0, 1);
+        read_w(1, 1);
+      } else if constexpr (m > 4 * NJ && K % NJ == 0 && I + 1 < 4) {
+        read_w(I + 1, 1);
       }
-      asm volatile("" : "+a"(acc[K / 4][K % 4]));
-      mfma_range<K, K + 1>(acc, fw, fa, swv, sav);
-      asm volatile("" : "+a"(acc[K / 4][K % 4]));
+      asm volatile("" : "+a"(acc[K / NJ][K % NJ]));
+      mfma_range<K, K + 1, NJ>(acc, fw, fa, swv, sav);
+      asm volatile("" : "+a"(acc[K / NJ][K % NJ]));
       __builtin_amdgcn_sched_barrier(0);
     };
-    read_half(0);
+    read_a(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_w(i, 0);
     if constexpr (MODE == 0) {
-      static_for<0, 32>(mfma_at);
+      static_for<0, kMfmas>(mfma_at);
     } else {
       static_for<0, kPure>(mfma_at);
-      static_for<0, 8>([&](auto gc) __attribute__((always_inline)) {
+      static_for<0, NG>([&](auto gc) __attribute__((always_inline)) {
         constexpr int g = decltype(gc)::value;
-        quant_group(rs, gc, na, (kb + 1) & 1, [&](auto kc) __attribute__((always_inline)) {
+        // the tables of stage kb+1 came before its W DMA; in MODE 2 that is
+        // the last DMA issued (MODE 1 waited for everything at its start)
+        quant_group(rs, gc, na, (kb + 1) & 1, ic<MODE == 2 ? kWDma : 0>{}, [&](auto kc) __attribute__((always_inline)) {
           static_for<0, kPerGroup>([&](auto qc) __attribute__((always_inline)) {
             constexpr int q = decltype(qc)::value;
             if constexpr (hook_of(kPerGroup, q) == decltype(kc)::value) mfma_at(ic<kPure + g * kPerGroup + q>{});
@@ -537,11 +549,11 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   };
 
   // ---- prologue: positions, the tile's W scales, stage 0 quantised, stage 1 on its way
-  if constexpr (ROPE) {
-    const int64_t pp = p.pos[min(t0 + tid, p.T - 1)];
-    spos[tid] = (pp >= 0 && pp < p.max_pos) ? static_cast<int32_t>(pp) : -1;
-  }
-  {
+  if (tid < kTile) {
+    if constexpr (ROPE) {
+      const int64_t pp = p.pos[min(t0 + tid, p.T - 1)];
+      spos[tid] = (pp >= 0 && pp < p.max_pos) ? static_cast<int32_t>(pp) : -1;
+    }
     // thread tid stages W row tid's scale bytes of all stages
     const uint8_t* scw = p.sw + (static_cast<size_t>(g) * p.N + n0 + min(tid, limW)) * KB;
     for (int s = 0; s < KB; ++s) wsc[s][tid >> 7][tid & 31][(tid >> 5) & 3] = scw[s];
@@ -550,7 +562,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   stage_barrier();                                   // spos is written
   if constexpr (ROPE) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) bad_rows |= (spos[arow0 + 8 * j] < 0 ? 1u : 0u) << j;
+    for (int j = 0; j < NG; ++j) bad_rows |= (spos[arow0 + 8 * j] < 0 ? 1u : 0u) << j;
   }
   load_a(0);
   issue_cs(sa0, 0);
@@ -582,7 +594,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   auto iter = [&](uint8_t* cw, uint8_t* ca, uint8_t* na, int kb) __attribute__((always_inline)) {
     step(ic<2>{}, cw, ca, na, kb);
     // stage kb+1's W has landed once at most stage kb+2's loads are pending
-    __builtin_amdgcn_s_waitcnt(wait_vm(kALoadsPerStage));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kALoads));
     stage_barrier();                                 // everyone is done with stage kb's buffers; stage kb+1 is in the other
     issue_cs(ca, kb + 2);
     issue_w(cw, kb + 2);
@@ -598,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
   }
   if (kb + 1 < KB) {                                 // kb = KB - 2
     // stage kb+1's BF16 and tables have landed once at most its W DMA is pending
-    __builtin_amdgcn_s_waitcnt(wait_vm(kWDmaPerStage));
+    __builtin_amdgcn_s_waitcnt(wait_vm(kWDma));
     step(ic<1>{}, (kb & 1) ? sw1 : sw0, (kb & 1) ? sa1 : sa0, (kb & 1) ? sa0 : sa1, kb);
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
     stage_barrier();
@@ -609,8 +621,8 @@ __global__ __launch_bounds__(256, 1) void woa_fused_kernel(FusedArgs p) {
 
   // ---- epilogue straight from the accumulators (as bmm_large_kernel)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + wt * 128 + j * 32 + r32;
+  for (int j = 0; j < NJ; ++j) {
+    const int t = t0 + wt * 32 * NJ + j * 32 + r32;
     uint16_t* orow = p.out + (static_cast<size_t>(t) * p.G + g) * p.N;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -665,12 +677,13 @@ mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* 
   p.total_tiles = p.tiles_t * p.tiles_n * G;
   p.per_xcd = (p.total_tiles + 7) / 8;
   const int grid = p.per_xcd * 8;
+  constexpr int nw = WOA_WAVES;
   if (rope_dim == 0)
-    woa_fused_kernel<false, false><<<grid, 256, 0, stream>>>(p);
+    woa_fused_kernel<nw, false, false><<<grid, 64 * nw, 0, stream>>>(p);
   else if (neox)
-    woa_fused_kernel<true, true><<<grid, 256, 0, stream>>>(p);
+    woa_fused_kernel<nw, true, true><<<grid, 64 * nw, 0, stream>>>(p);
   else
-    woa_fused_kernel<true, false><<<grid, 256, 0, stream>>>(p);
+    woa_fused_kernel<nw, true, false><<<grid, 64 * nw, 0, stream>>>(p);
   return launch_status("mx_wo_a_fused");
 }
 
