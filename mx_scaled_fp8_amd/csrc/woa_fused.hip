@@ -185,9 +185,12 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
   constexpr int kWDma = kTile / (8 * NW);          // W DMA instructions per wave and stage
   constexpr int kALoads = 2 * NG;                  // A loads per wave and stage
   constexpr int kMfmas = 8 * NJ;                   // MFMAs per wave and stage (two K-halves)
-  constexpr int kPure = kMfmas / 2;                // MFMAs of a stage before its quantisation work
+#ifndef WOA_PURE_DIV
+#define WOA_PURE_DIV 4
+#endif
+  constexpr int kPure = WOA_PURE_DIV == 0 ? 0 : kMfmas / WOA_PURE_DIV;   // MFMAs of a stage before its quantisation work
   constexpr int kPerGroup = (kMfmas - kPure) / NG; // MFMAs with each row group
-  static_assert(kPerGroup == 2, "two MFMAs per row group");
+  static_assert(kPerGroup * NG + kPure == kMfmas && kPerGroup >= 1 && kPerGroup <= 4, "MFMAs per row group");
   // stage buffers 0 and 1: W tile 256 x 128 B (sw) and A tile 256 x 128 B
   // (sa), four separate arrays so that the compiler can tell the weight DMA
   // from the activation codes and tables (with one array per stage it made
@@ -431,8 +434,13 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
     between(ic<0>{});
     m = max8(m);
     const bool finite = m < 0x7F80u;
-    const int e = e8m0_exponent<8>(finite ? m : 0);
-    const float sbits = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
+    // the E8M0 byte, e8m0_exponent<8>(m) + 127 for a finite amax, in three
+    // operations: with 0x1F added the mantissa field carries into the
+    // exponent field exactly when it exceeds 0x60, so the byte is
+    // ((m + 0x1F) >> 7) - 8, clamped at 0; the subtraction of 8 << 7 goes
+    // first and the shift is arithmetic
+    const int eb = max(static_cast<int>(m - 0x3E1u) >> 7, 0);
+    const float sbits = __uint_as_float(static_cast<uint32_t>(eb) << 23);
     between(ic<1>{});
     uint2 q0 = encode8(v0, sbits), q1 = encode8(v1, sbits);
     // a non-finite group: codes 0x7F (a blend with an opaque mask, which the
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
     between(ic<2>{});
     *reinterpret_cast<uint2*>(ba + qoff[0][j & 1] + j * 8 * kBK) = q0;
     *reinterpret_cast<uint2*>(ba + qoff[1][j & 1] + j * 8 * kBK) = q1;
-    (&asc[sb][0][0][0])[sc_index(j)] = static_cast<uint8_t>(finite ? e + 127 : 0xFF);
+    (&asc[sb][0][0][0])[sc_index(j)] = static_cast<uint8_t>(finite ? eb : 0xFF);
     between(ic<3>{});
   };
   auto quantise = [&](int kb, uint8_t* ba, int sb) __attribute__((always_inline)) {
