@@ -57,9 +57,6 @@ constexpr int kOpBytes = kTile * kBK;       // 32 KiB per operand per stage
 constexpr int kMaxKB = 32;                  // K <= 4096: the W scales of a tile stay in LDS
 constexpr int kFmtFp8 = 0;
 
-#ifndef WOA_WAVES
-#define WOA_WAVES 8
-#endif
 
 constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
 template <int N>
@@ -74,7 +71,8 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<B + 1, E>(f);
   }
 }
-// MFMA q (0, 1) of a row group is issued at point 2q (0..3) of the group's work
+// MFMA q of a row group is issued at point hook_of(per_group, q) (0..3) of
+// the group's work: 0 and 2 for two MFMAs per group, else 0, 1, 2, ...
 constexpr int hook_of(int per_group, int q) { return per_group == 2 ? 2 * q : q; }
 
 struct FusedArgs {
@@ -185,10 +183,7 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
   constexpr int kWDma = kTile / (8 * NW);          // W DMA instructions per wave and stage
   constexpr int kALoads = 2 * NG;                  // A loads per wave and stage
   constexpr int kMfmas = 8 * NJ;                   // MFMAs per wave and stage (two K-halves)
-#ifndef WOA_PURE_DIV
-#define WOA_PURE_DIV 4
-#endif
-  constexpr int kPure = WOA_PURE_DIV == 0 ? 0 : kMfmas / WOA_PURE_DIV;   // MFMAs of a stage before its quantisation work
+  constexpr int kPure = kMfmas / 4;                // MFMAs of a stage before its quantisation work
   constexpr int kPerGroup = (kMfmas - kPure) / NG; // MFMAs with each row group
   static_assert(kPerGroup * NG + kPure == kMfmas && kPerGroup >= 1 && kPerGroup <= 4, "MFMAs per row group");
   // stage buffers 0 and 1: W tile 256 x 128 B (sw) and A tile 256 x 128 B
@@ -685,7 +680,7 @@ mx_status launch_woa_fused(const void* x, const int64_t* positions, const void* 
   p.total_tiles = p.tiles_t * p.tiles_n * G;
   p.per_xcd = (p.total_tiles + 7) / 8;
   const int grid = p.per_xcd * 8;
-  constexpr int nw = WOA_WAVES;
+  constexpr int nw = 8;   // two waves per SIMD (4 waves of 128 x 128: about 12% slower)
   if (rope_dim == 0)
     woa_fused_kernel<nw, false, false><<<grid, 64 * nw, 0, stream>>>(p);
   else if (neox)
