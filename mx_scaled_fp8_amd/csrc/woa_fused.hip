@@ -10,31 +10,31 @@
 // with q, sa exactly the quantiser's (OCP codes; the result of an FNUZ run
 // is the same), fp32 accumulation, BF16 out.
 //
-// Design: the 256 (t) x 256 (n) tiles, 4 waves of 128 x 128 and
-// v_mfma_scale_f32_32x32x64_f8f6f4 of bmm_large_kernel, one tile per
-// workgroup, K-steps of 128.  A 128-wide K-step of a token row is exactly one
-// quantisation group, so each stage quantises whole groups:
-//  * A arrives as BF16 in registers: 8 lanes per token row, each lane two
-//    16-byte chunks (a, a + d) of the row's 256-byte stage slice, 8 rows per
-//    load instruction (two instructions per 8 rows, 16 per wave per stage);
+// Design: one 256 (t) x 256 (n) tile per workgroup, 8 waves (two per SIMD)
+// of 64 t x 128 n on v_mfma_scale_f32_32x32x64_f8f6f4, K-steps of 128.  A
+// 128-wide K-step of a token row is exactly one quantisation group, so each
+// stage quantises whole groups:
+//  * A arrives as BF16 in registers by buffer loads, two stages ahead: each
+//    wave quantises 32 of the tile's rows, 8 lanes per row, each lane two
+//    16-byte chunks (a, a + d) of the row's 256-byte stage slice;
 //  * a stage that holds the last 128 dims of a head rotates its last R dims
 //    (R <= 64; fp32, products and sums rounded one by one, BF16 nearest
 //    even): with d = 8 the interleaved pairs lie inside a chunk, with
 //    d = R/16 the split-half pairs (i, i + R/2) are the lane's two chunks;
-//    the tokens' cos/sin rows come by LDS-DMA into the stage's A buffer,
+//    the tokens' cos/sin rows come by LDS-DMA into the stage's A slot,
 //    each where its token's codes will go;
 //  * the group amax is a packed-u16 max over the lane's 16 values and three
 //    DPP steps over the row's 8 lanes; the E8M0 byte is integer arithmetic on
 //    its bits; the codes come from v_cvt_scalef32_pk_fp8_bf16 (the
 //    quantiser's instructions, so the codes are the quantiser's);
-//  * codes go to the stage's A buffer in LDS (the swizzled layout the MFMA
-//    fragment reads use), scale bytes to a per-stage A-scale slot;
+//  * codes go to the stage's A slot in LDS (the swizzled layout the MFMA
+//    fragment reads use), scale bytes to a per-buffer A-scale array;
 //  * W goes global -> LDS by LDS-DMA as in bmm_large_kernel.
-// Per stage: the MFMAs of stage kb from LDS; meanwhile this wave quantises
-// stage kb+1 from its registers into the other buffer and loads stage kb+2's
-// BF16; one barrier; then the W DMA of stage kb+2 into the buffer stage kb
-// used.  A token whose position is outside the table gets NaN scales (its
-// outputs are NaN), as from the quantiser.
+// Per stage: the MFMAs of stage kb from LDS, with the quantisation of stage
+// kb+1 (into the other A slot) and the loads of stage kb+2's BF16 placed
+// between them; one barrier; then the W DMA of stage kb+2 into the slot
+// stage kb used.  A token whose position is outside the table gets NaN
+// scales (its outputs are NaN), as from the quantiser.
 #include <algorithm>
 #include <type_traits>
 
@@ -56,8 +56,6 @@ constexpr int kBK = 128;                    // K bytes of FP8 per stage = one qu
 constexpr int kOpBytes = kTile * kBK;       // 32 KiB per operand per stage
 constexpr int kMaxKB = 32;                  // K <= 4096: the W scales of a tile stay in LDS
 constexpr int kFmtFp8 = 0;
-
-
 constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
 template <int N>
 using ic = std::integral_constant<int, N>;
