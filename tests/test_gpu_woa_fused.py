@@ -124,3 +124,34 @@ def test_declined_shapes_and_empty():
     e = mx.mx_wo_a_fused(x[:0], pos[:0], cs, cs, 16, 512, 64, w2, s2)
     assert e.shape == (0, 2, 16)
     assert mx.mx_get_counters()["wo_a_fused"] == 0
+
+
+@pytest.mark.parametrize("style", [INTERLEAVED, NEOX])
+def test_repeated_launches_match_the_two_kernel_path(style):
+    """Eight rope stages per group and 64 tiles: every launch gives the same
+    bits, and those agree with the quantiser followed by the GEMM (the same
+    codes and scales, sums in another order) within the GEMM bound.  A
+    rotation that read its tables before their DMA landed would show here as
+    launch-to-launch differences or as large errors."""
+    rng = np.random.default_rng(77 + (style == NEOX))
+    T, Gn, N, H, D, R = 1024, 16, 512, 128, 512, 64
+    K = H * D // Gn
+    x = dev_u16(workloads.activations(rng, T, H * D))
+    pos = dev_i64(rng.integers(0, 8192, T))
+    cos, sin = workloads.rope_tables(rows=8192, rope_dim=R)
+    cos, sin = dev_u16(cos), dev_u16(sin)
+    w = dev_u8(workloads.weight_codes(rng, (Gn, N, K)))
+    ws = dev_u8(workloads.scale_bytes(rng, (Gn, N, K // 128), -8, -4))
+    say("fused wo_a repeated launches", style)
+    outs = [mx.mx_wo_a_fused(x, pos, cos, sin, H, D, R, w, ws, STYLE[style]) for _ in range(3)]
+    q, s = mx.mx_inv_rope_group_quant(x, pos, cos, sin, H, D, R, STYLE[style])
+    two = mx.mx_bmm_a8w8_mxscale(q.view(T, Gn, K), s.view(T, Gn, K // 128), w, ws)
+    torch.cuda.synchronize()
+    first = outs[0].view(torch.int16)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), first)
+    a = outs[0].float().cpu().numpy()
+    b = two.float().cpu().numpy().reshape(a.shape)
+    assert np.isfinite(a).all()
+    rms = float(np.sqrt(np.mean(b.astype(np.float64) ** 2)))
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-3 * rms)
