@@ -4,7 +4,9 @@ MX-scale GEMM in one kernel) against the oracle's quantise-then-GEMM result:
 the oracle's codes and scales.  Cases: the tiny wo_a problem (both pairings),
 shapes crossing every tile edge (T, N past 256; several groups; K from one
 stage to 32; D of 128 to 512; rope_dim 0 to 128), the decode batch on every
-row, tokens with positions outside the table, and the shapes it declines.
+row, tokens with positions outside the table, the shapes it declines, a
+seeded sweep of 16 shapes, and repeated launches (bit-identical, and within
+the bound of the quantiser-then-GEMM path).
 The prefill chunk is checked on every output in test_gpu_full_prefill.py."""
 
 import numpy as np
@@ -155,3 +157,38 @@ def test_repeated_launches_match_the_two_kernel_path(style):
     assert np.isfinite(a).all()
     rms = float(np.sqrt(np.mean(b.astype(np.float64) ** 2)))
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.abs(b) + 1e-3 * rms)
+
+
+def _sweep_cases():
+    """A seeded sweep: T from 1 to 700, 1 to 4 groups, N up to 640, heads of
+    128 to 512 dims, K = H*D/G from one stage to 32, rope_dim 0 to 64 in both
+    pairings (NeoX only at 16, 32, 64)."""
+    rng = np.random.default_rng(5150)
+    cases = []
+    while len(cases) < 16:
+        Gn = int(rng.integers(1, 5))
+        D = 128 * int(rng.integers(1, 5))
+        H = int(rng.integers(1, 9))
+        if (H * D) % Gn or (H * D // Gn) % 128 or H * D // Gn > 4096:
+            continue
+        style = NEOX if rng.integers(0, 2) else INTERLEAVED
+        R = int(rng.choice([0, 16, 32, 64])) if style == NEOX else 16 * int(rng.integers(0, 5))
+        T = int(rng.integers(1, 701))
+        N = 16 * int(rng.integers(1, 41))
+        cases.append((len(cases), T, Gn, N, H, D, R, style))
+    return cases
+
+
+@pytest.mark.parametrize("case,T,Gn,N,H,D,R,style", _sweep_cases())
+def test_sweep(case, T, Gn, N, H, D, R, style):
+    rng = np.random.default_rng(900 + case)
+    K = H * D // Gn
+    x = workloads.activations(rng, T, H * D)
+    pos = rng.integers(0, 4096, T)
+    w = workloads.weight_codes(rng, (Gn, N, K))
+    ws = workloads.scale_bytes(rng, (Gn, N, K // 128), -8, -4)
+    cos, sin = workloads.rope_tables(rows=4096, rope_dim=max(R, 16))
+    say("fused wo_a sweep", case, T, Gn, N, H, D, R, style)
+    got = _run(x, pos, cos, sin, H, D, R, w, ws, style)
+    ref = _ref(x, pos, cos, sin, H, D, R, w, ws, style)
+    assert_gemm_close(got.reshape(ref.shape), ref, f"sweep {case}: T={T} G={Gn} N={N} H={H} D={D} R={R} {style}")
