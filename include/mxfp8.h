@@ -177,7 +177,8 @@ mx_status mx_bmm_a8w8_mxscale(const uint8_t* a, const uint8_t* a_scale, int32_t 
  * K <= 4096, D % 128 == 0, rope_dim % 16 == 0 and rope_dim <= min(D, 64)
  * (split halves: rope_dim in {16, 32, 64}), N >= 1 with N % 16 == 0,
  * x, w, out, cos and sin 16-byte aligned, positions 8-byte aligned,
- * max_pos >= 1 when rope_dim > 0.  Other shapes return MX_ERR_UNSUPPORTED
+ * max_pos >= 1 when rope_dim > 0.  Other shapes, and tables of 2 GiB or
+ * more (max_pos * rope_dim >= 2^31 bytes each), return MX_ERR_UNSUPPORTED
  * (the two calls serve them).
  */
 mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos,

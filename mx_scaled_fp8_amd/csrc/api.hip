@@ -248,11 +248,12 @@ mx_status mx_wo_a_fused(const void* x, const int64_t* positions, const void* cos
            rope_style);
   // shapes the one-kernel path does not take: the two calls serve them
   if (K > 4096 || D % 128 != 0 || rope_dim > 64 ||
-      (rope_style == MX_ROPE_NEOX && rope_dim > 0 && (rope_dim & (rope_dim - 1)) != 0))
+      (rope_style == MX_ROPE_NEOX && rope_dim > 0 && (rope_dim & (rope_dim - 1)) != 0) ||
+      (rope_dim > 0 && max_pos > (int64_t(0x7FFFFFFF) / rope_dim)))
     return fail(MX_ERR_UNSUPPORTED,
-                "%s: K = %lld, D = %d, rope_dim = %d (style %d) not served in one kernel; use "
+                "%s: K = %lld, D = %d, rope_dim = %d (style %d), max_pos = %lld not served in one kernel; use "
                 "mx_inv_rope_group_quant then mx_bmm_a8w8_mxscale",
-                fn, (long long)K, D, rope_dim, rope_style);
+                fn, (long long)K, D, rope_dim, rope_style, (long long)max_pos);
   if (T == 0) { clear_error(); return MX_OK; }
   MX_CHECK(x && w && w_scale && out, "%s: null tensor pointer", fn);
   MX_CHECK(aligned(x, 16) && aligned(w, 16) && aligned(out, 16), "%s: x, w and out must be 16-byte aligned", fn);

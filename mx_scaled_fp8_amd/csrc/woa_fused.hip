@@ -29,7 +29,7 @@
 //    quantiser's instructions, so the codes are the quantiser's);
 //  * codes go to the stage's A slot in LDS (the swizzled layout the MFMA
 //    fragment reads use), scale bytes to a per-buffer A-scale array;
-//  * W goes global -> LDS by LDS-DMA as in bmm_large_kernel.
+//  * W goes global -> LDS by LDS-DMA (buffer loads) as in bmm_large_kernel.
 // Per stage: the MFMAs of stage kb from LDS, with the quantisation of stage
 // kb+1 (into the other A slot) and the loads of stage kb+2's BF16 placed
 // between them; one barrier; then the W DMA of stage kb+2 into the slot
@@ -219,7 +219,11 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
     return kr >= KB ? kr - KB : kr;
   };
 
-  // ---- W: LDS-DMA of the stage's 256 rows (rows past N re-read the last one)
+  // ---- W: LDS-DMA of the stage's 256 rows (rows past N re-read the last one).
+  // Every LDS-DMA here is a buffer load: with a global (flat-encoded) LDS-DMA
+  // in flight the compiler waits for all vector memory before the first use of
+  // any loaded register, which would hold each stage's quantisation until the
+  // weight DMA issued just before it had landed.
   const int dma_row = wave * 8 + (lane >> 3);
   const uint32_t dma_chunk = static_cast<uint32_t>((lane & 7) ^ swz8(dma_row)) * 16;
   const uint8_t* baseW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
@@ -227,14 +231,18 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
   // lane offset of row group 0 and the cap past which rows re-read the last one
   const uint32_t offW0 = static_cast<uint32_t>(dma_row) * static_cast<uint32_t>(p.K) + dma_chunk;
   const uint32_t capW = static_cast<uint32_t>(limW) * static_cast<uint32_t>(p.K) + dma_chunk;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(baseW), 0, static_cast<int>(static_cast<uint32_t>(limW + 1) * static_cast<uint32_t>(p.K)),
+      kBufferFlags);
   auto issue_w = [&](uint8_t* bw, int kb) __attribute__((always_inline)) {
-    const uint8_t* bW = baseW + static_cast<uint32_t>(real_stage(kb)) * kBK;
+    const int so = real_stage(kb) * kBK;
 #pragma unroll
     for (int it = 0; it < kWDma; ++it) {
       uint32_t b = offW0;
       asm volatile("" : "+v"(b));                    // formed per issue, not held as 8 addresses
       const uint32_t o = min(b + static_cast<uint32_t>(it * 8 * NW) * static_cast<uint32_t>(p.K), capW);
-      __builtin_amdgcn_global_load_lds(bW + o, (lds_void_t*)(bw + (it * 8 * NW + wave * 8) * kBK), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(bw + (it * 8 * NW + wave * 8) * kBK), 16,
+                                               static_cast<int>(o), so, 0, 0);
     }
   };
 
@@ -316,9 +324,15 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
   // the stage's codes are written there), each at the 128 bytes its token's
   // codes will take: cos[R/2] then sin[R/2] (R <= 64).  A wave loads and
   // reads only its own rows, and a row's codes are written after its
-  // rotation has read its tables, so no barrier is involved.  One DMA
-  // instruction per row group: 8 lanes (16-byte pieces) per row, 8 rows;
-  // pieces past the 2R bytes re-read the first (never used).
+  // rotation has read its tables, so no barrier is involved.  Two DMA
+  // instructions per row group (cos, then sin R bytes further on),
+  // 8 rows, the R/16 lanes of a row's pieces enabled.  The tables are read
+  // through buffer resources (the host keeps max_pos * R below 2^31).
+  const uint32_t tab_bytes = static_cast<uint32_t>(p.max_pos * R);
+  const __amdgpu_buffer_rsrc_t cres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.cos), 0, static_cast<int>(tab_bytes), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t sres =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.sin), 0, static_cast<int>(tab_bytes), kBufferFlags);
   auto issue_cs = [&](uint8_t* ba, int kb) __attribute__((always_inline)) {
     if (!ROPE || !rope_stage(kb)) return;
     uint8_t* dst = ba + wave * kRowsPerWave * kBK;
@@ -327,12 +341,13 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
 #pragma unroll
     for (int k = 0; k < NG; ++k) {
       int tr = wave * kRowsPerWave + k * 8 + (lane >> 3);   // tile row
-      asm volatile("" : "+v"(tr));                   // read here, not hoisted as 8 live positions and pointers
+      asm volatile("" : "+v"(tr));                   // read here, not hoisted as 8 live positions
       const int pj = max(spos[tr], 0);               // outside the table: row 0 (its codes are NaN)
-      const uint16_t* src = piece < npc ? p.cos + static_cast<int64_t>(pj) * half + piece * 8
-                          : piece < 2 * npc ? p.sin + static_cast<int64_t>(pj) * half + (piece - npc) * 8
-                                            : p.cos + static_cast<int64_t>(pj) * half;
-      __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(dst + k * 1024), 16, 0, 0);
+      const int off = pj * R + piece * 16;
+      if (piece < npc) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(cres, (lds_void_t*)(dst + k * 1024), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void_t*)(dst + k * 1024 + npc * 16), 16, off, 0, 0, 0);
+      }
     }
   };
 

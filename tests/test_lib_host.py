@@ -151,6 +151,30 @@ def test_quant_validation(dry):
     assert _quant(style=1, cos=FAKE + 8) == mx.MX_ERR_INVALID_ARG       # split halves read 16 bytes
 
 
+def _fused(**kw):
+    a = dict(x=FAKE, pos=FAKE, cos=FAKE, sin=FAKE, max_pos=100, T=16, H=128, D=512, R=64, style=0, w=FAKE,
+             sw=FAKE, out=FAKE, G=16, N=1024)
+    a.update(kw)
+    return _call("mx_wo_a_fused", a["x"], a["pos"], a["cos"], a["sin"], a["max_pos"], a["T"], a["H"], a["D"],
+                 a["R"], a["style"], a["w"], a["sw"], a["out"], a["G"], a["N"], None)
+
+
+def test_wo_a_fused_validation(dry):
+    assert _fused() == mx.MX_OK
+    assert _fused(T=0, x=None, out=None) == mx.MX_OK                     # empty is a no-op
+    assert _fused(R=0, pos=None, cos=None, sin=None) == mx.MX_OK
+    for bad in (dict(T=-1), dict(H=0), dict(G=3), dict(N=100), dict(R=8), dict(style=2), dict(x=None),
+                dict(out=FAKE + 2), dict(pos=None), dict(max_pos=0), dict(cos=FAKE + 4)):
+        assert _fused(**bad) == mx.MX_ERR_INVALID_ARG, bad
+    # shapes the one kernel does not take; the two calls serve them
+    for unsupported in (dict(G=8),                                      # K = 8192
+                        dict(R=128), dict(R=48, style=1),
+                        dict(max_pos=(1 << 31) // 64),                  # 2 GiB cos table
+                        dict(R=16, max_pos=1 << 27)):
+        assert _fused(**unsupported) == mx.MX_ERR_UNSUPPORTED, unsupported
+    assert _fused(max_pos=(1 << 31) // 64 - 1) == mx.MX_OK             # just under 2 GiB
+
+
 def _bmm(**kw):
     a = dict(a=FAKE, sa=FAKE, fmt=0, w=FAKE, sw=FAKE, out=FAKE, T=64, G=16, N=1024, K=4096)
     a.update(kw)
