@@ -80,6 +80,11 @@ static_assert(wait_vm(0) == 0x0070 && wait_vm(16) == 0x4070 && wait_vm(18) == 0x
                   wait_vm(32) == 0x8070 && kWaitLgkmOnly == 0xC07F && wait_vm_only(8) == 0x0F78,
               "s_waitcnt encoding");
 
+// Word 3 of a raw buffer resource (gfx9 layout): 32-bit data format, no
+// swizzle, no thread-id offset.  With stride 0 a load reads base + vector
+// offset + scalar offset, and offsets at or past num_records read zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 __device__ __forceinline__ uint32_t div_u32(uint32_t n, DivU32 dv) {
   return dv.magic == 0 ? n : static_cast<uint32_t>(__umul64hi(static_cast<uint64_t>(n), dv.magic));
 }

@@ -57,24 +57,29 @@ __device__ __forceinline__ v8i make_frag(const uint4 lo, const uint4 hi) {
 // The weight slice [16 rows][K] into sW as [step][row][128 B] and its scale
 // rows [16][K/32] into sS, by LDS-DMA.  Operand instruction ii moves rows
 // 8(ii % 2)..8(ii % 2)+7 of step ii / 2 (1 KiB); wave w issues ii = w, w+4,
-// ...  The scale rows move 4 bytes per lane.
+// ...  The scale rows move 4 bytes per lane (the slice's scale rows are one
+// contiguous range).  The DMA is issued as buffer loads: with a global
+// (flat-encoded) LDS-DMA in flight the compiler waits for all vector memory
+// before the first use of any loaded register, so a kernel could not work
+// on x while the weight is on its way.
 __device__ __forceinline__ void dma_weight_slice(const uint8_t* w, const uint8_t* sw, int n0, int K, uint8_t* sW,
                                                  uint8_t* sS, int wave, int lane) {
   const int KB = K / kStep, SPK = K / 32;
   const int dr = lane >> 3;
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(w + static_cast<size_t>(n0) * K), 0, kRowsN * K, kBufferFlags);
   for (int ii = wave; ii < 2 * KB; ii += 4) {
     const int kt = ii >> 1, half = ii & 1, r = 8 * half + dr;
-    const uint8_t* src = w + static_cast<size_t>(n0 + r) * K + kt * kStep + ((lane & 7) ^ swz(r)) * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(sW + kt * kStepBytes + 8 * half * kStep), 16, 0, 0);
+    const int off = r * K + kt * kStep + ((lane & 7) ^ swz(r)) * 16;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(sW + kt * kStepBytes + 8 * half * kStep), 16, off, 0,
+                                             0, 0);
   }
   const int sc_bytes = kRowsN * SPK;
+  const __amdgpu_buffer_rsrc_t sres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(sw + static_cast<size_t>(n0) * SPK), 0, sc_bytes, kBufferFlags);
   for (int jj = wave; jj * 256 < sc_bytes; jj += 4) {
     const int byte = jj * 256 + 4 * lane;
-    if (byte < sc_bytes) {
-      const int r = byte / SPK, off = byte - r * SPK;
-      __builtin_amdgcn_global_load_lds(sw + static_cast<size_t>(n0 + r) * SPK + off, (lds_void_t*)(sS + jj * 256), 4,
-                                       0, 0);
-    }
+    if (byte < sc_bytes) __builtin_amdgcn_raw_ptr_buffer_load_lds(sres, (lds_void_t*)(sS + jj * 256), 4, byte, 0, 0, 0);
   }
 }
 

@@ -60,7 +60,6 @@ constexpr int kWaitVmMax = kWaitLgkmOnly;  // LDS traffic only
 template <int N>
 using ic = std::integral_constant<int, N>;
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr int kBufferFlags = 0x00020000;    // buffer resource word 3 (gfx9): 32-bit data format, no swizzle
 // calls f(ic<k>) for k = B .. E-1, in order
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
