@@ -581,8 +581,10 @@ __global__ __launch_bounds__(256, 1) void bmm_persistent_kernel(LargeArgs p) {
     dW = p.w + (static_cast<size_t>(g) * p.N + n0) * p.K;
     dA = p.a + static_cast<size_t>(t0) * rowA + static_cast<size_t>(g) * p.K;
     dkb0 = kb0;
-    capW = static_cast<uint32_t>(p.N - 1 - n0) * static_cast<uint32_t>(p.K) + dma_chunk;
-    capA = static_cast<uint32_t>(p.T - 1 - t0) * rowA + dma_chunk;
+    // the caps count at most a tile's rows: (T - 1 - t0) * rowA itself can
+    // pass 2^32 (T * G * K >= 4 GiB) and would wrap to a cap inside the tile
+    capW = static_cast<uint32_t>(min(p.N - 1 - n0, kLN - 1)) * static_cast<uint32_t>(p.K) + dma_chunk;
+    capA = static_cast<uint32_t>(min(p.T - 1 - t0, kLT - 1)) * rowA + dma_chunk;
   };
   auto issue = [&](uint8_t* buf, int kb) {   // kb < KB
     int kr = kb + dkb0;

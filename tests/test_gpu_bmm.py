@@ -309,3 +309,31 @@ def test_five_chunks_in_one_call():
     ra, rsa = a[idx].cpu().numpy(), sa[idx].cpu().numpy()
     del a, sa, out
     assert_gemm_close(got, G.bmm_a8w8_mxscale(ra, rsa, w, sw), "T=40960 one call")
+
+
+@pytest.mark.slow
+def test_activation_rows_past_4gib():
+    """T = 65793 in one launch: the activations span 4.31 GB, so for the
+    token tile at t0 = 256 the distance to the last row, (T - 1 - t0) rows of
+    G*K bytes, is exactly 2^32 bytes.  The persistent kernel caps its row
+    offsets at the tile's last valid row; a cap computed from that distance
+    in 32 bits wraps to 0 and every row of the tile would read row 256.
+    Sampled rows of that tile and around the other 2^32 multiples are checked
+    against the oracle."""
+    T, Gn, N, K = 65793, 16, 1024, 4096
+    assert ((T - 1 - 256) * Gn * K) == 2 ** 32
+    say("bmm one call T=65793 G=16 N=1024 K=4096")
+    _, _, w, sw = workloads.gemm_operands(657, 1, Gn, N, K)
+    gen = torch.Generator(device="cuda").manual_seed(657)
+    a = torch.randint(0, 256, (T, Gn, K), dtype=torch.uint8, device="cuda", generator=gen)
+    a[(a & 0x7F) == 0x7F] = 0x7E
+    sa = torch.randint(115, 126, (T, Gn, K // 128), dtype=torch.uint8, device="cuda", generator=gen)
+    out = mx.mx_bmm_a8w8_mxscale(a, sa, dev_u8(w), dev_u8(sw))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 256, 257, 300, 400, 511, 512, 65535, 65536, 65537, 65791, T - 1],
+                                     np.random.default_rng(657).integers(256, 512, 8)]))
+    idx = torch.from_numpy(rows).cuda()
+    got = host_u16(out[idx].contiguous())
+    ra, rsa = a[idx].cpu().numpy(), sa[idx].cpu().numpy()
+    del a, sa, out
+    assert_gemm_close(got, G.bmm_a8w8_mxscale(ra, rsa, w, sw), "T=65793 one call")
