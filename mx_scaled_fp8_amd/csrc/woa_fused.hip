@@ -211,7 +211,12 @@ __global__ __launch_bounds__(64 * NW, 1) void woa_fused_kernel(FusedArgs p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wt = wave >> 1;
   const int KB = p.K / kBK;                        // <= kMaxKB
-  const int kb0 = (tt + nt) % KB;                  // K rotation, as bmm_large_kernel
+  // K rotation by token tile only: the tile's 4 n-tiles (neighbouring
+  // workgroups of one XCD) read each stage's BF16 activation rows at about
+  // the same time, so the rows come from HBM once and from L2 for the rest
+  // (with the n-tiles a stage apart, as in bmm_large_kernel, 2.0-2.4 GB were
+  // fetched per prefill chunk against 1.47 GB)
+  const int kb0 = tt % KB;
   const int L = p.G * p.K;                         // elements per token row (H * D)
   auto real_stage = [&](int kb) __attribute__((always_inline)) {
     int kr = kb + kb0;
