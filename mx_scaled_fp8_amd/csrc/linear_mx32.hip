@@ -273,9 +273,8 @@ __global__ __launch_bounds__(256, 1) void linear_mx32_fused_kernel(FusedArgs p) 
 
   dma_weight_slice(p.w, p.sw, n0, p.K, sW, sS, wave, lane);
 
-  // ---- quantise x into MFMA fragments.  (The compiler waits for all vector
-  // memory before the first use of x, the weight's DMA included; with a
-  // quarter of K per wave what follows is a few hundred instructions.)
+  // ---- quantise x into MFMA fragments while the weight's DMA is in flight
+  // (its buffer-load form lets the compiler wait for the x loads alone)
   v8i xf[SPW];
   int xsb[SPW];
 #pragma unroll
